@@ -1,0 +1,190 @@
+"""CPU oracle for the fused add + argmax readout (ctypes front of ``oracle.c``).
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only ``tests/``, the package smoke
+check and the benchmark's CPU-baseline leg import this module.  It shares no
+code with the GPU library and the GPU library never calls it.
+
+The arithmetic lives in ``oracle.c`` (plain single-threaded C); this file only
+builds it with gcc when no build is present and marshals numpy arrays.  What
+the oracle computes is stated in the header comment of ``oracle.c``, with the
+passages of the XPress kernels page it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+_U16P = ctypes.POINTER(ctypes.c_uint16)
+_I64P = ctypes.POINTER(ctypes.c_int64)
+
+
+def build(force: bool = True) -> str:
+    """Compile ``oracle.c`` to ``liboracle.so`` with plain gcc (no fast-math,
+    no FMA contraction) and return the library path."""
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+           "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_bf16_to_double.restype = ctypes.c_double
+        lib.oracle_bf16_from_double.argtypes = [ctypes.c_double]
+        lib.oracle_bf16_from_double.restype = ctypes.c_uint16
+        lib.oracle_bf16_sum.argtypes = [ctypes.c_uint16, ctypes.c_uint16]
+        lib.oracle_bf16_sum.restype = ctypes.c_uint16
+        lib.oracle_bf16_sum_many.argtypes = [_U16P, _U16P, _U16P, ctypes.c_int64]
+        lib.oracle_bf16_sum_many.restype = None
+        lib.oracle_bf16_sum_grid.argtypes = [_U16P, ctypes.c_int64, _U16P]
+        lib.oracle_bf16_sum_grid.restype = None
+        lib.oracle_add_argmax_row.argtypes = [_U16P, _U16P, ctypes.c_int64]
+        lib.oracle_add_argmax_row.restype = ctypes.c_int64
+        lib.oracle_add_argmax_to_blk.argtypes = [
+            _U16P, _U16P, _I64P] + [ctypes.c_int64] * 5
+        lib.oracle_add_argmax_to_blk.restype = ctypes.c_int
+        lib.oracle_add_argmax_rows.argtypes = [
+            _U16P, _U16P, _I64P] + [ctypes.c_int64] * 5
+        lib.oracle_add_argmax_rows.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def _u16(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("expected bf16 bit patterns as uint16, got %s" % a.dtype)
+    return a
+
+
+def _p16(a: np.ndarray):
+    return a.ctypes.data_as(_U16P)
+
+
+def bf16_to_double(h: int) -> float:
+    """Exact value of one bf16 bit pattern."""
+    return _load().oracle_bf16_to_double(int(h) & 0xFFFF)
+
+
+def bf16_from_double(x: float) -> int:
+    """Nearest bf16 (ties to even) of a binary64 value, as a bit pattern."""
+    return int(_load().oracle_bf16_from_double(float(x)))
+
+
+def bf16_sum(a: int, b: int) -> int:
+    """bf16(a + b) of two bf16 bit patterns."""
+    return int(_load().oracle_bf16_sum(int(a) & 0xFFFF, int(b) & 0xFFFF))
+
+
+def bf16_sum_many(a, b) -> np.ndarray:
+    """Element-wise bf16(a + b) over two equal-shape uint16 arrays."""
+    a = _u16(a)
+    b = _u16(b)
+    if a.shape != b.shape:
+        raise ValueError("shape mismatch")
+    out = np.empty(a.shape, dtype=np.uint16)
+    _load().oracle_bf16_sum_many(_p16(a), _p16(b), _p16(out), a.size)
+    return out
+
+
+def bf16_sum_grid(a_vals) -> np.ndarray:
+    """``out[i, b] = bf16(a_vals[i] + b)`` for all 65536 patterns b."""
+    a_vals = _u16(a_vals).reshape(-1)
+    out = np.empty((a_vals.size, 65536), dtype=np.uint16)
+    _load().oracle_bf16_sum_grid(_p16(a_vals), a_vals.size, _p16(out))
+    return out
+
+
+def add_argmax_row(base_row, bias_row) -> int:
+    """First index of the maximum of bf16(base_row + bias_row)."""
+    a = _u16(base_row).reshape(-1)
+    b = _u16(bias_row).reshape(-1)
+    if a.size != b.size or a.size < 1:
+        raise ValueError("rows must be non-empty and of equal length")
+    return int(_load().oracle_add_argmax_row(_p16(a), _p16(b), a.size))
+
+
+def _check_layout(buf: np.ndarray, rows: int, V: int, stride: int, name: str):
+    if stride < V:
+        raise ValueError("%s row stride %d < V=%d" % (name, stride, V))
+    need = (rows - 1) * stride + V if rows > 0 else 0
+    if buf.size < need:
+        raise ValueError("%s holds %d elements, layout needs %d" % (name, buf.size, need))
+
+
+def add_argmax_to_blk(base, bias, blk: np.ndarray, N: int, B: int, V: int,
+                      stride_base_r: int, stride_bias_r: int) -> None:
+    """In-place oracle readout on host arrays; same argument meaning as the
+    GPU entry point.  ``blk`` must be a C-contiguous int64 array of N*B."""
+    base = _u16(base)
+    bias = _u16(bias)
+    if blk.dtype != np.int64 or not blk.flags.c_contiguous or blk.size != N * B:
+        raise ValueError("blk must be a C-contiguous int64 array of N*B elements")
+    rows = N * (B - 1)
+    _check_layout(base, rows, V, stride_base_r, "base")
+    _check_layout(bias, rows, V, stride_bias_r, "bias")
+    rc = _load().oracle_add_argmax_to_blk(
+        _p16(base), _p16(bias), blk.ctypes.data_as(_I64P),
+        N, B, V, stride_base_r, stride_bias_r)
+    if rc != 0:
+        raise ValueError("oracle rejected the layout")
+
+
+def add_argmax_rows(base, bias, r0: int, r1: int, V: int, stride_base_r: int,
+                    stride_bias_r: int) -> np.ndarray:
+    """Argmax of rows [r0, r1) as an int64 array (no blk scatter)."""
+    base = _u16(base)
+    bias = _u16(bias)
+    _check_layout(base, r1, V, stride_base_r, "base")
+    _check_layout(bias, r1, V, stride_bias_r, "bias")
+    out = np.empty(max(r1 - r0, 0), dtype=np.int64)
+    rc = _load().oracle_add_argmax_rows(
+        _p16(base), _p16(bias), out.ctypes.data_as(_I64P), r0, r1, V,
+        stride_base_r, stride_bias_r)
+    if rc != 0:
+        raise ValueError("oracle rejected the layout")
+    return out
+
+
+def add_argmax_rows_threaded(base, bias, rows: int, V: int, stride_base_r: int,
+                             stride_bias_r: int, threads: int) -> np.ndarray:
+    """The same per-row oracle, rows split evenly over ``threads`` host
+    threads (ctypes releases the GIL during each call)."""
+    base = _u16(base)
+    bias = _u16(bias)
+    out = np.empty(rows, dtype=np.int64)
+    threads = max(1, min(int(threads), rows if rows > 0 else 1))
+    bounds = [rows * t // threads for t in range(threads + 1)]
+
+    def work(t):
+        r0, r1 = bounds[t], bounds[t + 1]
+        out[r0:r1] = add_argmax_rows(base, bias, r0, r1, V, stride_base_r,
+                                     stride_bias_r)
+
+    ts = [threading.Thread(target=work, args=(t,)) for t in range(threads)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    return out

@@ -1,0 +1,210 @@
+/*
+ * oracle.c -- plain, slow CPU oracle for the fused add + argmax readout.
+ *
+ * TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the package
+ * smoke check and the benchmark's CPU-baseline leg may load this library.  It
+ * shares no code, header, table or helper with the GPU library: the GPU path
+ * never includes, links or calls it, and it never calls the GPU path.
+ *
+ * What it computes (XPress kernels page, "fused_add_argmax_to_blk" and the two
+ * stage kernels "_xpress_add_argmax_partial_kernel" and
+ * "_xpress_add_argmax_reduce_to_blk_kernel"):
+ *
+ *   for every draft row r = n*(B-1) + b   (0 <= n < N, 0 <= b < B-1)
+ *     s_v = bf16( base[r, v] + bias[r, v] ),  v = 0 .. V-1
+ *     blk[n, 1 + b] = lowest v with s_v == max_u s_u
+ *   blk[n, 0] (the verified anchor) and every other byte are left alone.
+ *
+ * Readings where the pages leave a step open (each one is listed with its
+ * reason in the design notes):
+ *   - the sum is the exact sum of the two bf16 values rounded once to bf16
+ *     with round-to-nearest, ties-to-even (the stage-1 kernel rounds the sum to
+ *     the input dtype; the top-C kernel widens to fp32 first and says the
+ *     full-vocab path does the same).  Here the sum is formed in binary64 and
+ *     then rounded to bf16 by an explicit integer-grid rounding written below.
+ *     binary64 carries 53 >= 2*8+2 significant bits, so rounding first to
+ *     binary64 and then to bf16 gives the same bf16 as rounding the exact sum
+ *     once (the double-rounding innocuity bound for addition);
+ *   - subnormal bf16 values are kept, never flushed;
+ *   - values compare as real numbers: -0 equals +0;
+ *   - on equal maxima the lowest vocabulary index wins (what an argmax over
+ *     the chunk followed by a strict ">" scan over chunks in ascending order
+ *     yields);
+ *   - NaN inputs are outside the contract; a NaN sum never wins here.
+ *
+ * Everything is single-threaded and unvectorised on purpose.
+ */
+#include <math.h>
+#include <stdint.h>
+
+/* ---------------------------------------------------------------------------
+ * bf16 decoding, from the field definition.
+ *
+ * A bf16 is 1 sign bit, 8 exponent bits (bias 127) and 7 fraction bits.
+ *   exponent 0      : subnormal, value = fraction * 2^-133   (2^-126 * f/128)
+ *   exponent 1..254 : normal,    value = (128 + fraction) * 2^(e - 127 - 7)
+ *   exponent 255    : infinity (fraction 0) or NaN.
+ * Every bf16 value is exactly representable in binary64.
+ * ------------------------------------------------------------------------- */
+double oracle_bf16_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 7) & 0xFF;
+    int f = h & 0x7F;
+    double mag;
+    if (e == 0xFF) {
+        mag = (f == 0) ? INFINITY : NAN;
+    } else if (e == 0) {
+        mag = ldexp((double)f, -133);
+    } else {
+        mag = ldexp((double)(128 + f), e - 127 - 7);
+    }
+    return sign ? -mag : mag;
+}
+
+/* ---------------------------------------------------------------------------
+ * Round a binary64 value to the nearest bf16, ties to even (IEEE 754
+ * roundTiesToEven), keeping subnormals and overflowing to infinity.
+ *
+ * The bf16 values in the binade [2^k, 2^(k+1)) (k >= -126) are the integer
+ * multiples of the quantum q = 2^(k-7); below 2^-126 the quantum stays at
+ * 2^-133 (the subnormal range).  So: pick q, scale x by 1/q (exact, q is a
+ * power of two), round that real number to an integer with ties going to the
+ * even integer, scale back.  A result of magnitude >= 2^128 is infinity
+ * (the value rounded as if the exponent were unbounded exceeds the largest
+ * finite bf16).
+ * ------------------------------------------------------------------------- */
+uint16_t oracle_bf16_from_double(double x)
+{
+    if (isnan(x)) {
+        return 0x7FC0; /* a quiet NaN; outside the contract */
+    }
+    uint16_t sign = signbit(x) ? 0x8000 : 0x0000;
+    double a = fabs(x);
+    if (a == 0.0) {
+        return sign; /* +0 or -0 as given */
+    }
+    if (isinf(a)) {
+        return sign | 0x7F80;
+    }
+    int e2;
+    (void)frexp(a, &e2);  /* a = m * 2^e2, m in [0.5, 1) */
+    int k = e2 - 1;       /* a in [2^k, 2^(k+1)) */
+    if (k > 127) {
+        return sign | 0x7F80; /* at least 2^128: beyond every finite bf16 */
+    }
+    if (k < -126) {
+        k = -126; /* subnormal range shares the smallest normal quantum */
+    }
+    double scaled = ldexp(a, 7 - k); /* a / q, exact */
+    double lo = floor(scaled);
+    double frac = scaled - lo;       /* exact: scaled < 2^53 */
+    double m = lo;
+    if (frac > 0.5) {
+        m = lo + 1.0;
+    } else if (frac == 0.5) {
+        /* halfway: take the even neighbour */
+        m = (fmod(lo, 2.0) == 0.0) ? lo : lo + 1.0;
+    }
+    /* m is an integer in [0, 256]: 256 means the value rounded up into the
+     * next binade, whose significand is 128 with the exponent one higher. */
+    if (m >= 256.0) {
+        m = 128.0;
+        k += 1;
+    }
+    if (m == 0.0) {
+        return sign; /* cannot happen for a nonzero sum of bf16s; kept total */
+    }
+    if (m < 128.0) {
+        /* only possible at k == -126: a subnormal, exponent field 0 */
+        return sign | (uint16_t)m;
+    }
+    int efield = k + 127;
+    if (efield >= 0xFF) {
+        return sign | 0x7F80; /* overflow to infinity */
+    }
+    return sign | (uint16_t)(efield << 7) | (uint16_t)((int)m - 128);
+}
+
+/* The rounded sum of one pair: bf16(a + b), formed in binary64. */
+uint16_t oracle_bf16_sum(uint16_t a, uint16_t b)
+{
+    double s = oracle_bf16_to_double(a) + oracle_bf16_to_double(b);
+    return oracle_bf16_from_double(s);
+}
+
+/* Element-wise rounded sums of n pairs (used by the pins on the oracle). */
+void oracle_bf16_sum_many(const uint16_t* a, const uint16_t* b, uint16_t* out,
+                          int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        out[i] = oracle_bf16_sum(a[i], b[i]);
+    }
+}
+
+/* All rounded sums a_vals[i] + b for every one of the 65536 bf16 patterns b:
+ * out[i * 65536 + b].  Used for the exhaustive pin of the element rounding. */
+void oracle_bf16_sum_grid(const uint16_t* a_vals, int64_t n_a, uint16_t* out)
+{
+    for (int64_t i = 0; i < n_a; ++i) {
+        for (int64_t b = 0; b < 65536; ++b) {
+            out[i * 65536 + b] = oracle_bf16_sum(a_vals[i], (uint16_t)b);
+        }
+    }
+}
+
+/* Argmax of one row: the lowest v whose rounded sum equals the row maximum.
+ * The scan runs v = 0 .. V-1 and replaces the incumbent only on a strictly
+ * greater value, which is exactly "first maximum".  V >= 1. */
+int64_t oracle_add_argmax_row(const uint16_t* base_row, const uint16_t* bias_row,
+                              int64_t V)
+{
+    int64_t best_v = 0;
+    double best = oracle_bf16_to_double(oracle_bf16_sum(base_row[0], bias_row[0]));
+    for (int64_t v = 1; v < V; ++v) {
+        double s = oracle_bf16_to_double(oracle_bf16_sum(base_row[v], bias_row[v]));
+        if (s > best) {
+            best = s;
+            best_v = v;
+        }
+    }
+    return best_v;
+}
+
+/* The whole readout on host buffers.
+ *   base, bias : bf16 bit patterns, N*(B-1) rows, row strides in elements
+ *   blk        : int64 [N, B] row-major; blk[n*B + 1 + b] is written for
+ *                every row r = n*(B-1) + b; slot 0 is never touched.
+ * Returns 0, or -1 on arguments that describe no valid layout. */
+int oracle_add_argmax_to_blk(const uint16_t* base, const uint16_t* bias,
+                             int64_t* blk, int64_t N, int64_t B, int64_t V,
+                             int64_t stride_base_r, int64_t stride_bias_r)
+{
+    if (N < 0 || B < 1 || V < 1 || stride_base_r < V || stride_bias_r < V) {
+        return -1;
+    }
+    int64_t rows = N * (B - 1);
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t n = r / (B - 1);
+        int64_t b = r % (B - 1);
+        blk[n * B + 1 + b] = oracle_add_argmax_row(base + r * stride_base_r,
+                                                   bias + r * stride_bias_r, V);
+    }
+    return 0;
+}
+
+/* Rows [r0, r1) only, writing idx_out[r - r0]; lets a caller spread a large
+ * workload over several host threads without changing the arithmetic. */
+int oracle_add_argmax_rows(const uint16_t* base, const uint16_t* bias,
+                           int64_t* idx_out, int64_t r0, int64_t r1, int64_t V,
+                           int64_t stride_base_r, int64_t stride_bias_r)
+{
+    if (r0 < 0 || r1 < r0 || V < 1 || stride_base_r < V || stride_bias_r < V) {
+        return -1;
+    }
+    for (int64_t r = r0; r < r1; ++r) {
+        idx_out[r - r0] = oracle_add_argmax_row(base + r * stride_base_r,
+                                                bias + r * stride_bias_r, V);
+    }
+    return 0;
+}

@@ -1,0 +1,116 @@
+"""The oracle's pins must catch plausible mistakes in the oracle.
+
+Each case below rebuilds oracle.c with one deliberate mistake (a wrong
+comparison, a wrong rounding rule, a flushed subnormal, a wrong slot or row
+mapping, an ignored stride), loads the mutant on the CPU and checks that at
+least one pin fails on it.  Nothing here touches a GPU.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import exact_bf16
+from test_oracle import ARGMAX_ROWS, ROUNDING
+from vocab_wide_add_amd import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+U16P = ctypes.POINTER(ctypes.c_uint16)
+I64P = ctypes.POINTER(ctypes.c_int64)
+
+MUTATIONS = {
+    "last_max_wins": ("if (s > best) {", "if (s >= best) {"),
+    "ties_round_up": ("m = (fmod(lo, 2.0) == 0.0) ? lo : lo + 1.0;", "m = lo + 1.0;"),
+    "ties_round_down": ("m = (fmod(lo, 2.0) == 0.0) ? lo : lo + 1.0;", "m = lo;"),
+    "truncate": ("if (frac > 0.5) {", "if (frac > 2.0) {"),
+    "flush_subnormal_inputs": ("mag = ldexp((double)f, -133);", "mag = 0.0;"),
+    "wrong_exponent_bias": ("mag = ldexp((double)(128 + f), e - 127 - 7);",
+                            "mag = ldexp((double)(128 + f), e - 126 - 7);"),
+    "overflow_saturates": ("return sign | 0x7F80; /* overflow to infinity */",
+                           "return sign | 0x7F7F; /* overflow to infinity */"),
+    "anchor_overwritten": ("blk[n * B + 1 + b] =", "blk[n * B + b] ="),
+    "row_to_block_by_B": ("int64_t n = r / (B - 1);", "int64_t n = r / B;"),
+    "stride_ignored": ("oracle_add_argmax_row(base + r * stride_base_r,\n"
+                       "                                                   bias + r * stride_bias_r, V);",
+                       "oracle_add_argmax_row(base + r * V,\n"
+                       "                                                   bias + r * V, V);"),
+    "sign_dropped": ("return sign ? -mag : mag;", "return mag;"),
+}
+
+
+def _build_mutant(tmp_path, name):
+    old, new = MUTATIONS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation anchor for %s not unique/present" % name
+    path_c = os.path.join(tmp_path, "mut.c")
+    path_so = os.path.join(tmp_path, "libmut.so")
+    open(path_c, "w").write(src.replace(old, new))
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+                    "-w", "-o", path_so, path_c, "-lm"], check=True)
+    lib = ctypes.CDLL(path_so)
+    lib.oracle_bf16_sum.argtypes = [ctypes.c_uint16, ctypes.c_uint16]
+    lib.oracle_bf16_sum.restype = ctypes.c_uint16
+    lib.oracle_add_argmax_row.argtypes = [U16P, U16P, ctypes.c_int64]
+    lib.oracle_add_argmax_row.restype = ctypes.c_int64
+    lib.oracle_add_argmax_to_blk.argtypes = [U16P, U16P, I64P] + [ctypes.c_int64] * 5
+    lib.oracle_add_argmax_to_blk.restype = ctypes.c_int
+    return lib
+
+
+def _pins_pass(lib) -> bool:
+    for a, b, e, _ in ROUNDING:
+        if lib.oracle_bf16_sum(a, b) != e:
+            return False
+    for _, base, bias, idx, _ in ARGMAX_ROWS:
+        base = np.ascontiguousarray(base)
+        bias = np.ascontiguousarray(bias)
+        if lib.oracle_add_argmax_row(base.ctypes.data_as(U16P), bias.ctypes.data_as(U16P),
+                                     base.size) != idx:
+            return False
+    g = np.random.Generator(np.random.PCG64(1))
+    for _ in range(200):
+        V = int(g.integers(1, 24))
+        a = g.integers(0, 0x7F80, size=V).astype(np.uint16) | \
+            (g.integers(0, 2, size=V).astype(np.uint16) << 15)
+        b = g.integers(0, 0x7F80, size=V).astype(np.uint16) | \
+            (g.integers(0, 2, size=V).astype(np.uint16) << 15)
+        got = lib.oracle_add_argmax_row(a.ctypes.data_as(U16P), b.ctypes.data_as(U16P), V)
+        if got != exact_bf16.first_argmax(a, b):
+            return False
+    for (N, B, V, pad) in [(3, 5, 77, 9), (5, 3, 4097, 64)]:
+        base, bias, blk = workloads.planted(N, B, V, seed=V, pad=pad)
+        anchors = blk[:, 0].copy()
+        lib.oracle_add_argmax_to_blk(base.ctypes.data_as(U16P), bias.ctypes.data_as(U16P),
+                                     blk.ctypes.data_as(I64P), N, B, V, V + pad, V + pad)
+        want = (np.arange(N * (B - 1)) % V).reshape(N, B - 1)
+        if not np.array_equal(blk[:, 1:], want) or not np.array_equal(blk[:, 0], anchors):
+            return False
+    return True
+
+
+def test_unmutated_oracle_passes_the_pins(tmp_path):
+    # the same harness on the real source must pass, or the mutants prove nothing
+    src = open(SRC).read()
+    path_c = os.path.join(tmp_path, "orig.c")
+    path_so = os.path.join(tmp_path, "liborig.so")
+    open(path_c, "w").write(src)
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+                    "-o", path_so, path_c, "-lm"], check=True)
+    lib = ctypes.CDLL(path_so)
+    lib.oracle_bf16_sum.argtypes = [ctypes.c_uint16, ctypes.c_uint16]
+    lib.oracle_bf16_sum.restype = ctypes.c_uint16
+    lib.oracle_add_argmax_row.argtypes = [U16P, U16P, ctypes.c_int64]
+    lib.oracle_add_argmax_row.restype = ctypes.c_int64
+    lib.oracle_add_argmax_to_blk.argtypes = [U16P, U16P, I64P] + [ctypes.c_int64] * 5
+    lib.oracle_add_argmax_to_blk.restype = ctypes.c_int
+    assert _pins_pass(lib)
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutant_is_caught(tmp_path, name):
+    lib = _build_mutant(str(tmp_path), name)
+    assert not _pins_pass(lib), "pins did not catch mutation %r" % name

@@ -1,0 +1,172 @@
+"""Seeded synthetic inputs for the fused add + argmax readout.
+
+This module holds only random-number plumbing and buffer layout: it draws
+values, converts them to bf16 storage and lays rows out with their strides.  It
+contains none of the readout's arithmetic (no sums, no rounding of sums, no
+argmax), so the GPU path and the CPU oracle can both be fed from it.
+
+Shapes follow the XPress kernels page: a pass drafts B-1 slots in each of N
+blocks, the vocabulary is about 152k wide, and the materialised logits the
+fused readout avoids come to about 146 MB at N = 32, which at 2 bytes per bf16
+and V = 152064 pins B = 16 (480 draft rows).
+
+Recipe: ``numpy.random.SeedSequence(seed).spawn(3)`` gives three independent
+PCG64 streams -- one for base, one for bias, one for ids -- so that the first
+rows of a workload can be drawn without drawing the rest.  Draws:
+  1. base stream: ``rows x V`` values in row-major order -- float32 standard
+     normals times sigma, or integers uniform on the closed range [lo, hi];
+  2. bias stream: the same for bias, with its own sigma or range;
+  3. id stream: for workloads with a spike, one vocabulary id per row,
+     uniform on [0, V) (``spike`` is added to base at that id in float32,
+     before rounding to bf16); then the anchors, one id per block, uniform on
+     [0, V), stored in blk[:, 0].
+Float32 values become bf16 with torch's round-to-nearest-even conversion on
+the CPU; integer values in [-8, 8] are exact in bf16.  Rows are laid out with
+their row strides; every element between V and the stride (including after
+the last row) holds the poison value ``pad`` so that any read past V changes
+the answer.  blk slots 1..B-1 start at -1 so that a missing write shows.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional, Tuple
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    N: int
+    B: int
+    V: int
+    seed: int
+    base_dist: Tuple  # ("normal", sigma) or ("int", lo, hi)
+    bias_dist: Tuple
+    spike: Optional[float] = None
+    base_pad: int = 0  # row stride = V + pad (elements)
+    bias_pad: int = 0
+    pad_value: float = 100.0
+
+    @property
+    def rows(self) -> int:
+        return self.N * (self.B - 1)
+
+    @property
+    def stride_base(self) -> int:
+        return self.V + self.base_pad
+
+    @property
+    def stride_bias(self) -> int:
+        return self.V + self.bias_pad
+
+    @property
+    def bytes_read(self) -> int:
+        """Algorithmic bytes of one readout: two bf16 streams of rows x V."""
+        return self.rows * self.V * 4
+
+
+# The five synthetic workloads.  The names state what each one is.
+WORKLOADS = {
+    w.name: w
+    for w in [
+        # 6 rows, V not a multiple of any chunk width.
+        Workload("tiny_n2_b4_v1000", 2, 4, 1000, 0, ("normal", 4.0), ("normal", 0.5)),
+        # 56 rows of a 32k vocabulary.
+        Workload("small_n8_b8_v32000", 8, 8, 32000, 1, ("normal", 3.0), ("normal", 1.0)),
+        # The readout shape the pages size: 480 rows of a 152064 vocabulary,
+        # one +20 spike per row.
+        Workload("spike_n32_b16_v152064", 32, 16, 152064, 2, ("normal", 4.0),
+                 ("normal", 0.5), spike=20.0),
+        # Integer values in [-8, 8]: exact ties everywhere; padded row strides
+        # with +100 poison in the padding.
+        Workload("ties_strided_n32_b16_v151936", 32, 16, 151936, 3, ("int", -8, 8),
+                 ("int", -8, 8), base_pad=64, bias_pad=128),
+        # 3840 rows; bias wide enough that bf16 rounding of the sum often
+        # decides the winner.
+        Workload("large_n256_b16_v152064", 256, 16, 152064, 4, ("normal", 4.0),
+                 ("normal", 2.0)),
+    ]
+}
+
+# The workload the benchmark times by default (the pages' shape).
+BENCH_WORKLOAD = "spike_n32_b16_v152064"
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns via torch's CPU conversion (RNE)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _draw(g: np.random.Generator, dist: Tuple, shape) -> np.ndarray:
+    kind = dist[0]
+    if kind == "normal":
+        x = g.standard_normal(shape, dtype=np.float32)
+        x *= np.float32(dist[1])
+        return x
+    if kind == "int":
+        lo, hi = dist[1], dist[2]
+        return g.integers(lo, hi + 1, size=shape).astype(np.float32)
+    raise ValueError("unknown distribution %r" % (dist,))
+
+
+def _lay_out(bits: np.ndarray, stride: int, pad_bits: int) -> np.ndarray:
+    rows, V = bits.shape
+    out = np.full((rows, stride), pad_bits, dtype=np.uint16)
+    out[:, :V] = bits
+    return out
+
+
+def generate(w: Workload, rows_limit: Optional[int] = None):
+    """Build one workload on the host.
+
+    Returns ``(base, bias, blk)``: ``base`` is a uint16 array of shape
+    ``[rows, stride_base]`` holding bf16 bit patterns, ``bias`` likewise with
+    ``stride_bias``, and ``blk`` an int64 ``[N, B]`` array with the anchors in
+    column 0 and -1 elsewhere.  ``rows_limit`` draws only the first rows;
+    each buffer has its own stream filled row-major, so those rows are
+    identical to the full workload's first rows.
+    """
+    s_base, s_bias, s_ids = np.random.SeedSequence(w.seed).spawn(3)
+    g_ids = np.random.Generator(np.random.PCG64(s_ids))
+    rows, V = w.rows, w.V
+    keep = rows if rows_limit is None else min(rows, rows_limit)
+    base = _draw(np.random.Generator(np.random.PCG64(s_base)), w.base_dist, (keep, V))
+    if w.spike is not None:
+        ids = g_ids.integers(0, V, size=rows)[:keep]
+        base[np.arange(keep), ids] += np.float32(w.spike)
+    anchors = g_ids.integers(0, V, size=w.N)
+    pad_bits = int(f32_to_bf16_bits(np.array([w.pad_value], dtype=np.float32))[0])
+    base_bits = _lay_out(f32_to_bf16_bits(base), w.stride_base, pad_bits)
+    del base
+    bias = _draw(np.random.Generator(np.random.PCG64(s_bias)), w.bias_dist, (keep, V))
+    bias_bits = _lay_out(f32_to_bf16_bits(bias), w.stride_bias, pad_bits)
+    del bias
+    blk = np.full((w.N, w.B), -1, dtype=np.int64)
+    blk[:, 0] = anchors
+    return base_bits, bias_bits, blk
+
+
+def planted(N: int, B: int, V: int, seed: int = 0, pad: int = 0):
+    """Rows whose unique maximum sits at v = r mod V (r = draft row index).
+
+    Every element is a bf16 in [-4, 4) drawn on the grid of multiples of 1/16
+    (exact in bf16, and so are their sums); row r gets base = 64 at v = r mod V,
+    which no other element of the row can reach.  The expected readout is then
+    ``blk[n, 1 + b] = (n*(B-1) + b) mod V`` in closed form.
+    """
+    g = np.random.Generator(np.random.PCG64(seed))
+    rows = N * (B - 1)
+    base = (g.integers(-64, 64, size=(rows, V)) / 16.0).astype(np.float32)
+    bias = (g.integers(-64, 64, size=(rows, V)) / 16.0).astype(np.float32)
+    if rows:
+        base[np.arange(rows), np.arange(rows) % V] = 64.0
+    pad_bits = int(f32_to_bf16_bits(np.array([100.0], dtype=np.float32))[0])
+    base_bits = _lay_out(f32_to_bf16_bits(base), V + pad, pad_bits)
+    bias_bits = _lay_out(f32_to_bf16_bits(bias), V + pad, pad_bits)
+    blk = np.full((N, B), -1, dtype=np.int64)
+    blk[:, 0] = g.integers(0, V, size=N)
+    return base_bits, bias_bits, blk
