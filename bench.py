@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused add + argmax readout on one MI355X.
+
+One step = one call of ``xpress_add_argmax_to_blk`` over a whole batch of
+draft rows (every stage of the readout: stream loads, add + bf16 rounding,
+the (value, index) reduction, the cross-workgroup combine and the scatter
+into blk).  Inputs are resident in HBM before the timed region starts; the
+call rotates over several identical copies of the inputs whose total size
+exceeds twice the 256 MB last-level cache, so each call streams from HBM.
+
+Prints ONE JSON line.  ``value`` is effective HBM GB/s = rows * V * 4 bytes
+(two bf16 streams) per call over the wall time of the timed calls.
+``roofline.achieved`` uses the same algorithmic bytes over the average
+readout-kernel duration measured with HIP events on the launch stream.
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same rows
+on the host cores, and the GPU's answers for those rows are checked against
+it.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+LLC_BYTES = 256 * 2 ** 20    # MI355X Infinity Cache
+SRC = os.path.join(ROOT, "vocab_wide_add_amd", "csrc", "xpress_argmax.hip")
+
+
+def log(msg):
+    sys.stderr.write("[bench] %s\n" % msg)
+    sys.stderr.flush()
+
+
+def source_digest() -> str:
+    with open(SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_for(workload: str):
+    """HBM bytes per launch from committed PMC counter runs, if they were
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256") != source_digest():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(base, bias, w, target_s: float):
+    """The oracle, as is, on the first rows of the workload, rows spread over
+    the host cores.  Returns (result dict, rows checked, oracle answers)."""
+    import oracle
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    cores = max(1, min(cores, 64))
+    t0 = time.perf_counter()
+    oracle.add_argmax_rows(base, bias, 0, 1, w.V, w.stride_base, w.stride_bias)
+    t_row = max(time.perf_counter() - t0, 1e-4)
+    rows = int(min(w.rows, max(cores, target_s * cores / t_row)))
+    rows = max(1, rows)
+    t0 = time.perf_counter()
+    ans = oracle.add_argmax_rows_threaded(base, bias, rows, w.V, w.stride_base,
+                                          w.stride_bias, cores)
+    dt = time.perf_counter() - t0
+    gbs = rows * w.V * 4 / dt / 1e9
+    res = {"value": round(gbs, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+           "rows_per_s": round(rows / dt, 1),
+           "sample": "first %d of %d rows of %s, one pass, %.1f s" % (rows, w.rows, w.name, dt)}
+    return res, rows, ans
+
+
+def copy_probe(nbytes: int, reps: int):
+    """A plain device-to-device copy of known size (for scaling PMC counters)."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU work budget of the oracle baseline leg")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-bytes", type=int, default=0,
+                    help="only run a plain copy of this many bytes (PMC calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the readout has no cross-GPU step, and rows "
+              "shard across GPUs with no exchange; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from vocab_wide_add_amd import native, workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_probe_bytes:
+        copy_probe(args.copy_probe_bytes, max(1, args.steps))
+        return
+
+    name = args.workload or workloads.BENCH_WORKLOAD
+    w = workloads.WORKLOADS[name]
+    log("generating %s" % name)
+    base, bias, blk0 = workloads.generate(w)
+    bytes_per_call = w.bytes_read
+    footprint = base.nbytes + bias.nbytes
+    sets = max(1, math.ceil(2 * LLC_BYTES / footprint) + 1)
+    log("uploading %d input sets of %.1f MB" % (sets, footprint / 1e6))
+    dev = []
+    b_cpu = torch.from_numpy(base.view(np.int16))
+    i_cpu = torch.from_numpy(bias.view(np.int16))
+    for _ in range(sets):
+        dev.append((b_cpu.cuda(), i_cpu.cuda(), torch.from_numpy(blk0).cuda()))
+    stream = torch.cuda.current_stream()
+    plan = native.xpress_describe_plan(dev[0][0], dev[0][1], w.N, w.B, w.V,
+                                       w.stride_base, w.stride_bias)
+    native.xpress_reserve(w.N, w.B, w.V, stream=stream)
+
+    def step(k):
+        b, i, blk = dev[k % sets]
+        native.xpress_add_argmax_to_blk(b, i, blk, w.N, w.B, w.V, w.stride_base,
+                                        w.stride_bias, stream=stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    # timed region: wall clock over K steps, and a HIP event pair around each
+    # launch on the launch stream for the per-kernel duration
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    log("timing %d steps" % args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        starts[k].record(stream)
+        step(k)
+        ends[k].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = sorted(s.elapsed_time(e) * 1e-3 for s, e in zip(starts, ends))
+    kavg = sum(durs) / len(durs)
+
+    # answers of the last set touched, for the check against the oracle
+    got = dev[(args.steps - 1) % sets][2].cpu().numpy()
+
+    ms_per_step = wall / args.steps * 1e3
+    value = bytes_per_call * args.steps / wall / 1e9
+    achieved = bytes_per_call / kavg / 1e9
+    traffic = traffic_for(name)
+    out = {
+        "metric": "effective HBM GB/s (+ % of peak) and rows/s, add+argmax N=%d B=%d V=%d"
+                  % (w.N, w.B, w.V),
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "N": w.N, "B": w.B, "V": w.V, "rows": w.rows,
+                   "stride_base": w.stride_base, "stride_bias": w.stride_bias,
+                   "bytes_per_step": bytes_per_call, "input_sets": sets,
+                   "plan": plan},
+        "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "rows_per_s": round(w.rows * args.steps / wall, 1),
+        "kernel_us": {"avg": round(kavg * 1e6, 3), "min": round(durs[0] * 1e6, 3),
+                      "p50": round(durs[len(durs) // 2] * 1e6, 3),
+                      "p90": round(durs[int(len(durs) * 0.9)] * 1e6, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline")
+        cb, nrows, ans = cpu_baseline(base, bias, w, args.cpu_seconds)
+        out["cpu_baseline"] = cb
+        flat = got[:, 1:].reshape(-1)[:nrows]
+        out["checked_rows"] = nrows
+        out["checked_equal"] = bool(np.array_equal(flat, ans))
+        if not out["checked_equal"]:
+            log("MISMATCH against the oracle on the sampled rows")
+    print(json.dumps(out))
+    sys.stdout.flush()
+
+
+if __name__ == "__main__":
+    main()

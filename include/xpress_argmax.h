@@ -1,0 +1,160 @@
+/*
+ * xpress_argmax.h -- C ABI of the MI355X (gfx950) fused add + argmax readout.
+ *
+ * The operation (XPress kernels page, "fused_add_argmax_to_blk" and its stage
+ * kernels "_xpress_add_argmax_partial_kernel" /
+ * "_xpress_add_argmax_reduce_to_blk_kernel"): one Jacobi pass drafts B-1 slots
+ * in each of N blocks; draft row r = n*(B-1) + b carries base logits and a
+ * refiner bias over a vocabulary of V ids, and the readout writes
+ *
+ *     blk[n, 1 + b] = argmax_v  bf16( base[r, v] + bias[r, v] )
+ *
+ * without ever storing the [N*(B-1), V] sum.  Each sum is formed from the two
+ * bf16 values and rounded once to bf16 (round-to-nearest, ties to even,
+ * subnormals kept) before the comparison, as the stage-1 kernel does by
+ * casting the sum back to the input dtype; values compare as reals (-0 equals
+ * +0) and the lowest vocabulary id wins a tie (the first-maximum argmax of a
+ * chunk followed by a strict ">" scan over chunks in ascending order).  Slot
+ * 0 of every block (the verified anchor) is never written; the next pass
+ * reads blk in place.  NaN inputs are outside the contract.
+ *
+ * Everything here is plain C: pointers, 64-bit sizes and a HIP stream.
+ * No function keeps a reference to a caller buffer after it returns.
+ */
+#ifndef XPRESS_ARGMAX_H
+#define XPRESS_ARGMAX_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+#define XPRESS_OK 0
+#define XPRESS_EINVAL 1   /* an argument describes no valid layout */
+#define XPRESS_EHIP 2     /* a HIP call failed; see xpress_last_hip_error() */
+#define XPRESS_ENOMEM 3   /* the library could not allocate its workspace */
+#define XPRESS_ECAPTURE 4 /* the workspace would have to grow while the stream
+                             is being captured into a graph; call
+                             xpress_reserve() before capturing */
+
+/*
+ * xpress_add_argmax_to_blk -- the fused readout (page and passages above).
+ *
+ *   base           device pointer to bf16 bit patterns, N*(B-1) rows; row r
+ *                  starts at base + r*stride_base_r and holds V elements with
+ *                  unit stride.  Read only.
+ *   bias           device pointer, the refiner bias, laid out like base with
+ *                  its own row stride.  Read only; may alias base.
+ *   blk            device pointer to int64 [N, B], row-major and contiguous.
+ *                  blk[n*B + 1 + b] receives the winning vocabulary id of row
+ *                  n*(B-1) + b; blk[n*B] and all other memory are untouched.
+ *                  Must not overlap base or bias.
+ *   N              blocks, >= 0.
+ *   B              slots per block (anchor + B-1 drafts), >= 1.
+ *   V              vocabulary size, 1 <= V <= 2^31 - 1.
+ *   stride_base_r  row stride of base in elements, >= V.
+ *   stride_bias_r  row stride of bias in elements, >= V.
+ *   stream         HIP stream the work is queued on (0 = the null stream).
+ *
+ * Asynchronous: returns once the kernels are queued; blk is valid after the
+ * stream reaches that point.  N == 0 or B == 1 (no draft rows) returns
+ * XPRESS_OK and queues nothing.  Any layout is accepted; rows whose starts
+ * and strides are 16-byte aligned take the vector path, others a scalar path
+ * with identical results.
+ *
+ * Errors: XPRESS_EINVAL for a negative N, B < 1, V out of range, a stride
+ * below V, a null pointer when there are rows, or blk overlapping an input
+ * (nothing is queued); XPRESS_ENOMEM / XPRESS_ECAPTURE when the workspace
+ * cannot be provided; XPRESS_EHIP when a launch fails.  Faults inside the
+ * kernels (e.g. a pointer to too small a buffer) surface at the caller's
+ * next synchronisation, as for any HIP kernel.
+ *
+ * Workspace: when the chosen plan splits a row over several workgroups the
+ * library uses a small device workspace of its own (about 12 bytes per row),
+ * one per (device, stream), allocated on first use and left zeroed by every
+ * call, so repeated calls and graph replays need no clearing.  Calls queued
+ * on different streams use different workspaces and may run concurrently.
+ * The caller keeps every buffer alive until the queued work has finished.
+ */
+int xpress_add_argmax_to_blk(const uint16_t* base, const uint16_t* bias,
+                             int64_t* blk, int64_t N, int64_t B, int64_t V,
+                             int64_t stride_base_r, int64_t stride_bias_r,
+                             hipStream_t stream);
+
+/*
+ * xpress_reserve -- pre-allocate the workspace the readout would use for
+ * (N, B, V) on `stream`'s device and stream, so that a later call -- e.g.
+ * one being captured into a HIP graph -- allocates nothing.  Synchronous.
+ * Returns XPRESS_OK, XPRESS_EINVAL, XPRESS_ENOMEM or XPRESS_EHIP.
+ */
+int xpress_reserve(int64_t N, int64_t B, int64_t V, hipStream_t stream);
+
+/*
+ * xpress_release -- free every workspace the library holds on the current
+ * device (after synchronising that device).  Optional; for tests and for
+ * callers that want the memory back.
+ */
+int xpress_release(void);
+
+/*
+ * Plan override, for tests and tuning.  combine selects how a row's partial
+ * results meet:
+ *   XPRESS_COMBINE_AUTO    the library's measured choice per shape;
+ *   XPRESS_COMBINE_SINGLE  one workgroup per row, no cross-workgroup step;
+ *   XPRESS_COMBINE_ATOMIC  several workgroups per row; each folds a packed
+ *                          64-bit (value, ~index) key into the row's slot with
+ *                          an atomic max, and the last to arrive writes blk
+ *                          and clears the slot (one launch);
+ *   XPRESS_COMBINE_TWO_PASS several workgroups per row write their packed key
+ *                          to a [rows, splits] table, a second small kernel
+ *                          reduces each row (two launches).
+ * splits is the number of workgroups per row (0 = automatic; ignored by
+ * SINGLE).  block_threads is the workgroup size (0 = automatic, else 64,
+ * 128, 256, 512 or 1024).  The setting is process-wide and applies to later
+ * calls.  Returns XPRESS_EINVAL for an unknown combine or block size.
+ */
+#define XPRESS_COMBINE_AUTO 0
+#define XPRESS_COMBINE_SINGLE 1
+#define XPRESS_COMBINE_ATOMIC 2
+#define XPRESS_COMBINE_TWO_PASS 3
+int xpress_set_plan(int combine, int splits, int block_threads);
+
+/*
+ * xpress_describe_plan -- what a call with these sizes and alignments would
+ * launch: *combine, *splits, *block_threads, *vector_path (1 = 16-byte loads)
+ * and *launches.  Pure host computation.  Returns XPRESS_OK or XPRESS_EINVAL.
+ */
+int xpress_describe_plan(const uint16_t* base, const uint16_t* bias, int64_t N,
+                         int64_t B, int64_t V, int64_t stride_base_r,
+                         int64_t stride_bias_r, int* combine, int* splits,
+                         int* block_threads, int* vector_path, int* launches);
+
+/*
+ * xpress_bf16_add_round_table -- the readout's element step alone, for
+ * checking it against the definition over every input pair.  For each i in
+ * [0, n_a) and each of the 65536 bf16 patterns b it writes
+ * out[i*65536 + b] = bf16(a_vals[i] + b) with the same device code the
+ * readout kernels use.  a_vals (n_a entries) and out (n_a*65536 entries) are
+ * device pointers.  Asynchronous on stream.  Returns XPRESS_OK,
+ * XPRESS_EINVAL (n_a < 0, null pointer) or XPRESS_EHIP.
+ */
+int xpress_bf16_add_round_table(const uint16_t* a_vals, int64_t n_a,
+                                uint16_t* out, hipStream_t stream);
+
+/* The HIP error code of the last failing HIP call on this thread. */
+int xpress_last_hip_error(void);
+
+/* A static, human-readable description of a status code. */
+const char* xpress_error_string(int status);
+
+/* Library version, "major.minor.patch". */
+const char* xpress_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XPRESS_ARGMAX_H */

@@ -1,0 +1,98 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point the
+header declares, and its host-only calls (plan description, plan override,
+error strings, argument validation ahead of any launch) behave as documented.
+No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from vocab_wide_add_amd import native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "xpress_argmax.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(xpress_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = native.load()
+    names = declared_functions()
+    assert "xpress_add_argmax_to_blk" in names and len(names) >= 8
+    for name in names:
+        assert hasattr(lib, name), name
+    # the binding keeps the same names
+    for name in names:
+        assert callable(getattr(native, name)), name
+
+
+def test_version_and_strings():
+    assert native.xpress_version() == "0.1.0"
+    for s in range(5):
+        assert native.xpress_error_string(s)
+    assert native.xpress_error_string(99) == "unknown status"
+
+
+def test_plan_for_the_pages_shape():
+    p = native.xpress_describe_plan(256, 256, 32, 16, 152064, 152064, 152064)
+    assert p["vector_path"] and p["launches"] == 1 and p["splits"] >= 2
+    p = native.xpress_describe_plan(258, 256, 32, 16, 152064, 152064, 152064)
+    assert not p["vector_path"]
+    p = native.xpress_describe_plan(256, 256, 32, 16, 152064, 152065, 152064)
+    assert not p["vector_path"]
+    p = native.xpress_describe_plan(256, 256, 0, 16, 152064, 152064, 152064)
+    assert p["launches"] == 0
+
+
+def test_plan_override_round_trip():
+    try:
+        native.xpress_set_plan(native.XPRESS_COMBINE_TWO_PASS, 5, 512)
+        p = native.xpress_describe_plan(256, 256, 2, 4, 100000, 100000, 100000)
+        assert (p["combine"], p["splits"], p["block_threads"], p["launches"]) == (
+            "two_pass", 5, 512, 2)
+        native.xpress_set_plan(native.XPRESS_COMBINE_SINGLE, 5, 64)
+        p = native.xpress_describe_plan(256, 256, 2, 4, 100000, 100000, 100000)
+        assert (p["combine"], p["splits"]) == ("single", 1)
+        with pytest.raises(native.XpressError):
+            native.xpress_set_plan(7, 0, 0)
+        with pytest.raises(native.XpressError):
+            native.xpress_set_plan(0, 0, 100)
+    finally:
+        native.xpress_set_plan(0, 0, 0)
+
+
+@pytest.mark.parametrize("args", [
+    (256, 256, 512, -1, 2, 8, 8, 8),       # N < 0
+    (256, 256, 512, 1, 0, 8, 8, 8),        # B < 1
+    (256, 256, 512, 1, 2, 0, 8, 8),        # V < 1
+    (256, 256, 512, 1, 2, 8, 7, 8),        # stride_base < V
+    (256, 256, 512, 1, 2, 8, 8, 7),        # stride_bias < V
+    (0, 256, 512, 1, 2, 8, 8, 8),          # null base with rows
+    (256, 0, 512, 1, 2, 8, 8, 8),          # null bias with rows
+    (256, 256, 0, 1, 2, 8, 8, 8),          # null blk with rows
+    (256, 4096, 260, 1, 2, 8, 8, 8),       # blk overlaps base
+    (4096, 256, 268, 1, 2, 8, 8, 8),       # blk overlaps bias
+    (256, 256, 512, 1, 2, 2 ** 31, 2 ** 31, 2 ** 31),  # V too large
+])
+def test_invalid_arguments_rejected_before_launch(args):
+    # validation happens before any HIP call, so this runs without a GPU
+    lib = native.load()
+    assert lib.xpress_add_argmax_to_blk(*args, None) == native.XPRESS_EINVAL
+
+
+def test_no_rows_is_ok_without_pointers():
+    lib = native.load()
+    assert lib.xpress_add_argmax_to_blk(0, 0, 0, 0, 16, 152064, 152064, 152064, None) == 0
+    assert lib.xpress_add_argmax_to_blk(0, 0, 0, 32, 1, 152064, 152064, 152064, None) == 0
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(native, "_lib", None)
+    monkeypatch.setattr(native, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(ImportError):
+        native.load()

@@ -1,0 +1,767 @@
+// xpress_argmax.hip -- fused add + argmax readout for MI355X (gfx950).
+//
+// The operation is the readout stage of one XPress Jacobi pass (XPress
+// kernels page, "fused_add_argmax_to_blk" and its two stage kernels): for
+// every draft row r = n*(B-1) + b,
+//     blk[n, 1 + b] = lowest v maximising bf16(base[r, v] + bias[r, v]),
+// with the [rows, V] sum never stored and slot 0 of each block untouched.
+//
+// Design (gfx950, wave64).  The work is a pure stream over 4 bytes per
+// element with ~8 VALU operations per element, so it is HBM-bound and has no
+// contraction in it -- no MFMA.  What matters is keeping enough 16-byte loads
+// in flight on every CU:
+//   * a row is split into `splits` contiguous vector ranges, one workgroup
+//     each; every lane streams 16-byte (8 x bf16) non-temporal loads of base
+//     and bias, UNROLL vectors of each in flight before any arithmetic;
+//   * element step: widen both bf16 to fp32 (a shift or a mask), one fp32
+//     add, one v_cvt_pk_bf16_f32 per pair (round-to-nearest-even, fp32
+//     denormals kept by the default kernel mode), widen back;
+//   * the lane keeps a running (max, vector id) per position 0..7 of the
+//     16-byte vector, replaced only on a strictly larger value -- vectors are
+//     visited in ascending order, so each position keeps its first maximum;
+//   * the 8 positions, then the 64 lanes (DPP quad_perm / row mirrors,
+//     ds_swizzle across 16, readlane across 32), then the waves (LDS) are
+//     merged in (value desc, index asc) order, which is the total order whose
+//     maximum is the first maximum;
+//   * the workgroups of a row meet in one of three ways (see
+//     xpress_set_plan in the header): a single workgroup per row, a packed
+//     64-bit key folded with an agent-scope atomic max plus an arrival count
+//     whose last arriver writes blk and clears the slot, or a key table plus
+//     a second small kernel.
+// The pages' own design (a [rows, chunks] fp32 + int64 scratch and a second
+// kernel per row) is the two-pass variant here, with one u64 key per chunk.
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "xpress_argmax.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr uint32_t kNoIndex = 0xFFFFFFFFu;  // "no candidate" (loses every tie)
+
+// ---------------------------------------------------------------------------
+// Element step.
+// ---------------------------------------------------------------------------
+
+// The low / high bf16 of a packed pair, widened to fp32 (exact: bf16 is the
+// upper half of binary32).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two element sums at once: a and b each pack two bf16; returns the two sums
+// rounded to bf16 (round-to-nearest-even), packed the same way.  The fp32 sum
+// of two bf16 values rounded to bf16 equals the exact sum rounded once to
+// bf16, since fp32 carries 24 >= 2*8 + 2 significant bits.
+__device__ __forceinline__ uint32_t add_round2(uint32_t a, uint32_t b)
+{
+    f32x2 s;
+    s.x = bf16_lo(a) + bf16_lo(b);
+    s.y = bf16_hi(a) + bf16_hi(b);
+    bf16x2 r = __builtin_convertvector(s, bf16x2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// Scalar form for the unaligned path and the vocabulary tail.
+__device__ __forceinline__ float add_round1(uint16_t a, uint16_t b)
+{
+    uint32_t p = add_round2((uint32_t)a, (uint32_t)b);
+    return bf16_lo(p);
+}
+
+// ---------------------------------------------------------------------------
+// (value, index) order: larger value first, then smaller index.  Float
+// comparison makes -0 equal to +0.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void merge(float& v, uint32_t& i, float ov, uint32_t oi)
+{
+    const bool take = (ov > v) | ((ov == v) & (oi < i));
+    v = take ? ov : v;
+    i = take ? oi : i;
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ void merge_dpp(float& v, uint32_t& i)
+{
+    float ov = __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+    uint32_t oi = dpp_u32<CTRL>(i);
+    merge(v, i, ov, oi);
+}
+
+// Reduce over the 64 lanes of the wave; the result is wave-uniform.
+__device__ __forceinline__ void wave_argmax(float& v, uint32_t& i)
+{
+    merge_dpp<0xB1>(v, i);   // quad_perm [1,0,3,2]: partner lane ^ 1
+    merge_dpp<0x4E>(v, i);   // quad_perm [2,3,0,1]: partner lane ^ 2
+    merge_dpp<0x141>(v, i);  // row_half_mirror: the other quad of each 8
+    merge_dpp<0x140>(v, i);  // row_mirror: the other 8 of each 16
+    // ds_swizzle bit mode, and_mask 0x1F, xor_mask 0x10: partner lane ^ 16
+    float ov = __uint_as_float((uint32_t)__builtin_amdgcn_ds_swizzle(
+        (int)__float_as_uint(v), 0x401F));
+    uint32_t oi = (uint32_t)__builtin_amdgcn_ds_swizzle((int)i, 0x401F);
+    merge(v, i, ov, oi);
+    // lanes 0..31 and 32..63 now each hold their half's result
+    float v0 = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 0));
+    uint32_t i0 = (uint32_t)__builtin_amdgcn_readlane((int)i, 0);
+    float v1 = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 32));
+    uint32_t i1 = (uint32_t)__builtin_amdgcn_readlane((int)i, 32);
+    merge(v0, i0, v1, i1);
+    v = v0;
+    i = i0;
+}
+
+// Workgroup reduction; every thread returns the workgroup's result.
+template <int T>
+__device__ __forceinline__ void block_argmax(float& v, uint32_t& i)
+{
+    constexpr int kWaves = T / 64;
+    wave_argmax(v, i);
+    if constexpr (kWaves > 1) {
+        __shared__ float sv[kWaves];
+        __shared__ uint32_t si[kWaves];
+        const int wave = threadIdx.x / 64;
+        if ((threadIdx.x & 63) == 0) {
+            sv[wave] = v;
+            si[wave] = i;
+        }
+        __syncthreads();
+        float bv = sv[0];
+        uint32_t bi = si[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) {
+            merge(bv, bi, sv[w], si[w]);
+        }
+        v = bv;
+        i = bi;
+        __syncthreads();  // sv/si may be reused by the next unit of work
+    }
+}
+
+// Packed order-preserving key: (ordered bf16 of the value) << 32 | ~index.
+// Unsigned order of keys == (value desc, index asc) order of candidates.
+// -0 is mapped to +0 first so the two compare equal.  A missing candidate
+// is the key 0, below every real key (real keys have ~index >= 2^31).
+__device__ __forceinline__ uint64_t make_key(float v, uint32_t i)
+{
+    if (i == kNoIndex) {
+        return 0;
+    }
+    uint32_t h = __float_as_uint(v) >> 16;  // v is a widened bf16
+    if (h == 0x8000u) {
+        h = 0;
+    }
+    uint32_t ord = (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
+    return ((uint64_t)ord << 32) | (uint64_t)(kNoIndex - i);
+}
+
+__device__ __forceinline__ int64_t key_index(uint64_t key)
+{
+    return (int64_t)(kNoIndex - (uint32_t)(key & 0xFFFFFFFFu));
+}
+
+// ---------------------------------------------------------------------------
+// Streaming parts.
+// ---------------------------------------------------------------------------
+
+// Vector path: vectors [q0, q1) of one row (a vector = 8 consecutive bf16 at
+// a 16-byte aligned address), strided over the T threads.  Returns the
+// thread's (value, index) candidate.
+template <int T, int UNROLL>
+__device__ __forceinline__ void scan_vectors(const u32x4* __restrict__ pa,
+                                             const u32x4* __restrict__ pb,
+                                             uint32_t q0, uint32_t q1,
+                                             float& out_v, uint32_t& out_i)
+{
+    float best[8];
+    uint32_t bq[8];
+    const uint32_t qfirst = q0 + threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        best[j] = -__builtin_inff();
+        bq[j] = qfirst;
+    }
+
+    auto consume = [&](const u32x4& va, const u32x4& vb, uint32_t q) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            uint32_t p = add_round2(va[w], vb[w]);
+            float s0 = bf16_lo(p);
+            float s1 = bf16_hi(p);
+            bool t0 = s0 > best[2 * w];
+            best[2 * w] = t0 ? s0 : best[2 * w];
+            bq[2 * w] = t0 ? q : bq[2 * w];
+            bool t1 = s1 > best[2 * w + 1];
+            best[2 * w + 1] = t1 ? s1 : best[2 * w + 1];
+            bq[2 * w + 1] = t1 ? q : bq[2 * w + 1];
+        }
+    };
+
+    uint32_t q = qfirst;
+    for (; q + (UNROLL - 1) * T < q1; q += UNROLL * T) {
+        u32x4 va[UNROLL], vb[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            va[u] = __builtin_nontemporal_load(pa + q + u * T);
+            vb[u] = __builtin_nontemporal_load(pb + q + u * T);
+        }
+        // keep every load of the batch ahead of the first use of any of them
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            consume(va[u], vb[u], q + u * T);
+        }
+    }
+    for (; q < q1; q += T) {
+        u32x4 va = __builtin_nontemporal_load(pa + q);
+        u32x4 vb = __builtin_nontemporal_load(pb + q);
+        consume(va, vb, q);
+    }
+
+    float v = -__builtin_inff();
+    uint32_t i = kNoIndex;
+    if (qfirst < q1) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            merge(v, i, best[j], bq[j] * 8u + (uint32_t)j);
+        }
+    }
+    out_v = v;
+    out_i = i;
+}
+
+// Scalar path: elements [e0, e1) of one row, strided over the T threads.
+template <int T>
+__device__ __forceinline__ void scan_scalars(const uint16_t* __restrict__ a,
+                                             const uint16_t* __restrict__ b,
+                                             uint32_t e0, uint32_t e1,
+                                             float& out_v, uint32_t& out_i)
+{
+    float best = -__builtin_inff();
+    uint32_t bi = kNoIndex;
+    uint32_t e = e0 + threadIdx.x;
+    if (e < e1) {
+        bi = e;
+    }
+    for (; e < e1; e += T) {
+        float s = add_round1(a[e], b[e]);
+        bool t = s > best;
+        best = t ? s : best;
+        bi = t ? e : bi;
+    }
+    out_v = best;
+    out_i = bi;
+}
+
+// ---------------------------------------------------------------------------
+// Kernels.
+// ---------------------------------------------------------------------------
+
+struct RowArgs {
+    const uint16_t* base;
+    const uint16_t* bias;
+    int64_t* blk;
+    int64_t stride_base;  // elements
+    int64_t stride_bias;  // elements
+    uint32_t rows;
+    uint32_t bm1;         // B - 1
+    uint32_t V;
+    uint32_t splits;      // workgroups per row
+    uint64_t* keys;       // ATOMIC: [rows] keys; TWO_PASS: [rows, splits] table
+    uint32_t* counts;     // ATOMIC: [rows] arrival counts
+};
+
+enum Combine { kSingle = XPRESS_COMBINE_SINGLE, kAtomic = XPRESS_COMBINE_ATOMIC,
+               kTwoPass = XPRESS_COMBINE_TWO_PASS };
+
+__device__ __forceinline__ void write_blk(const RowArgs& a, uint32_t row, int64_t idx)
+{
+    const uint32_t n = row / a.bm1;
+    const uint32_t b = row - n * a.bm1;
+    a.blk[(int64_t)n * (a.bm1 + 1) + 1 + b] = idx;
+}
+
+// One workgroup per (row, split) unit; the grid strides over units so any
+// number of rows fits in one launch.
+template <int T, int UNROLL, bool VEC, int COMBINE>
+__global__ __launch_bounds__(T) void readout_kernel(RowArgs a)
+{
+    const uint32_t units = a.rows * a.splits;
+    for (uint32_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+        const uint32_t row = unit / a.splits;
+        const uint32_t split = unit - row * a.splits;
+        const uint16_t* rb = a.base + (int64_t)row * a.stride_base;
+        const uint16_t* ri = a.bias + (int64_t)row * a.stride_bias;
+
+        float v;
+        uint32_t i;
+        if constexpr (VEC) {
+            const uint32_t nvec = a.V / 8u;
+            const uint32_t q0 = (uint32_t)(((uint64_t)split * nvec) / a.splits);
+            const uint32_t q1 = (uint32_t)(((uint64_t)(split + 1) * nvec) / a.splits);
+            scan_vectors<T, UNROLL>(reinterpret_cast<const u32x4*>(rb),
+                                    reinterpret_cast<const u32x4*>(ri), q0, q1, v, i);
+            // the last V % 8 elements belong to the row's last split
+            const uint32_t tail0 = nvec * 8u;
+            if (split == a.splits - 1 && tail0 + threadIdx.x < a.V) {
+                const uint32_t e = tail0 + threadIdx.x;
+                merge(v, i, add_round1(rb[e], ri[e]), e);
+            }
+        } else {
+            const uint32_t e0 = (uint32_t)(((uint64_t)split * a.V) / a.splits);
+            const uint32_t e1 = (uint32_t)(((uint64_t)(split + 1) * a.V) / a.splits);
+            scan_scalars<T>(rb, ri, e0, e1, v, i);
+        }
+
+        block_argmax<T>(v, i);
+
+        if (threadIdx.x == 0) {
+            if constexpr (COMBINE == kSingle) {
+                write_blk(a, row, (int64_t)i);
+            } else if constexpr (COMBINE == kTwoPass) {
+                a.keys[(uint64_t)row * a.splits + split] = make_key(v, i);
+            } else {
+                const uint64_t key = make_key(v, i);
+                if (key != 0) {
+                    __hip_atomic_fetch_max(&a.keys[row], key, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                }
+                // release: this workgroup's key is in before its arrival
+                // counts; acquire: the last arriver sees every key.
+                const uint32_t prev = __hip_atomic_fetch_add(
+                    &a.counts[row], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+                if (prev == a.splits - 1) {
+                    const uint64_t k = __hip_atomic_exchange(
+                        &a.keys[row], (uint64_t)0, __ATOMIC_RELAXED,
+                        __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(&a.counts[row], 0u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                    write_blk(a, row, key_index(k));
+                }
+            }
+        }
+    }
+}
+
+// Second pass of the two-pass combine: one thread per row reduces the row's
+// `splits` keys (a larger key is a larger value or, on equal values, a
+// smaller index) and writes blk.
+__global__ __launch_bounds__(256) void reduce_keys_kernel(RowArgs a)
+{
+    for (uint32_t row = blockIdx.x * 256u + threadIdx.x; row < a.rows;
+         row += gridDim.x * 256u) {
+        const uint64_t* k = a.keys + (uint64_t)row * a.splits;
+        uint64_t best = 0;
+        for (uint32_t s = 0; s < a.splits; ++s) {
+            best = k[s] > best ? k[s] : best;
+        }
+        write_blk(a, row, key_index(best));
+    }
+}
+
+// The element step over a table of pairs: out[i*65536 + b] = bf16(a_i + b).
+__global__ __launch_bounds__(256) void round_table_kernel(const uint16_t* __restrict__ a_vals,
+                                                          uint32_t n_a,
+                                                          uint32_t* __restrict__ out)
+{
+    // each thread makes one packed pair (b, b + 1) for one a
+    const uint64_t total = (uint64_t)n_a * 32768u;
+    for (uint64_t t = (uint64_t)blockIdx.x * 256u + threadIdx.x; t < total;
+         t += (uint64_t)gridDim.x * 256u) {
+        const uint32_t ia = (uint32_t)(t >> 15);
+        const uint32_t b0 = (uint32_t)(t & 32767u) * 2u;
+        const uint32_t av = a_vals[ia];
+        out[t] = add_round2(av | (av << 16), b0 | ((b0 + 1u) << 16));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e)
+{
+    g_last_hip_error = (int)e;
+    return XPRESS_EHIP;
+}
+
+struct Plan {
+    int combine;
+    int splits;
+    int threads;
+    bool vec;
+    int launches;
+};
+
+std::mutex g_plan_mu;
+int g_override_combine = XPRESS_COMBINE_AUTO;
+int g_override_splits = 0;
+int g_override_threads = 0;
+
+constexpr int kUnroll = 4;
+
+bool is_aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+Plan make_plan(const uint16_t* base, const uint16_t* bias, int64_t rows, int64_t V,
+               int64_t sb, int64_t sbi)
+{
+    Plan p;
+    p.vec = is_aligned16(base) && is_aligned16(bias) && (sb % 8 == 0) && (sbi % 8 == 0);
+    int oc, os, ot;
+    {
+        std::lock_guard<std::mutex> lk(g_plan_mu);
+        oc = g_override_combine;
+        os = g_override_splits;
+        ot = g_override_threads;
+    }
+    p.threads = ot ? ot : 256;
+    // Units of work a row can be cut into without starving a workgroup:
+    // at least two unrolled rounds of loads per thread.
+    const int64_t per_unit = (int64_t)p.threads * kUnroll * 2 * (p.vec ? 8 : 1);
+    int64_t max_splits = V / per_unit;
+    if (max_splits < 1) max_splits = 1;
+    // Aim for about 16 workgroups per CU over 256 CUs.
+    const int64_t target_units = 4096;
+    int64_t s = (target_units + rows - 1) / rows;
+    if (s > max_splits) s = max_splits;
+    if (s < 1) s = 1;
+    if (os > 0) s = os;
+    if (s > 65535) s = 65535;
+    // (row, split) units are counted in 32 bits on the device
+    if (s > 1 && rows * s > 0x7FFFFFFFll) s = 0x7FFFFFFFll / rows;
+    if (s < 1) s = 1;
+    p.splits = (int)s;
+    if (oc == XPRESS_COMBINE_AUTO) {
+        p.combine = (p.splits == 1) ? kSingle : kAtomic;
+    } else {
+        p.combine = oc;
+    }
+    if (p.combine == kSingle) p.splits = 1;
+    p.launches = (p.combine == kTwoPass) ? 2 : 1;
+    return p;
+}
+
+// Per (device, stream) workspace.  The atomic region ([rows] u64 keys and
+// [rows] u32 counts) is zero when idle: allocated zeroed, and every call's
+// last arriver clears what it used.  The table region is overwritten whole
+// by every two-pass call.
+struct Workspace {
+    uint64_t* keys = nullptr;
+    uint32_t* counts = nullptr;
+    int64_t rows_cap = 0;
+    uint64_t* table = nullptr;
+    int64_t table_cap = 0;
+};
+
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+int stream_capturing(hipStream_t stream, bool* capturing)
+{
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(stream, &st);
+    if (e != hipSuccess) return hip_fail(e);
+    *capturing = (st != hipStreamCaptureStatusNone);
+    return XPRESS_OK;
+}
+
+// Make sure the (device, stream) workspace holds `rows` atomic slots and a
+// `table` entry table; grows (synchronously) when needed.
+int ensure_workspace(hipStream_t stream, int64_t rows, int64_t table, Workspace** out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    Workspace& w = g_ws[std::make_pair(dev, stream)];
+    const bool grow_rows = rows > w.rows_cap;
+    const bool grow_table = table > w.table_cap;
+    if (grow_rows || grow_table) {
+        bool capturing = false;
+        int rc = stream_capturing(stream, &capturing);
+        if (rc != XPRESS_OK) return rc;
+        if (capturing) return XPRESS_ECAPTURE;
+        // the old buffers may still be in use by queued work on this stream
+        e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    if (grow_rows) {
+        int64_t cap = rows < 4096 ? 4096 : rows;
+        void* p = nullptr;
+        e = hipMalloc(&p, (size_t)cap * 12u);
+        if (e != hipSuccess) {
+            g_last_hip_error = (int)e;
+            return XPRESS_ENOMEM;
+        }
+        e = hipMemset(p, 0, (size_t)cap * 12u);
+        if (e != hipSuccess) {
+            (void)hipFree(p);
+            return hip_fail(e);
+        }
+        e = hipDeviceSynchronize();
+        if (e != hipSuccess) {
+            (void)hipFree(p);
+            return hip_fail(e);
+        }
+        if (w.keys) (void)hipFree(w.keys);
+        w.keys = static_cast<uint64_t*>(p);
+        w.counts = reinterpret_cast<uint32_t*>(static_cast<char*>(p) + (size_t)cap * 8u);
+        w.rows_cap = cap;
+    }
+    if (grow_table) {
+        int64_t cap = table < 65536 ? 65536 : table;
+        void* p = nullptr;
+        e = hipMalloc(&p, (size_t)cap * 8u);
+        if (e != hipSuccess) {
+            g_last_hip_error = (int)e;
+            return XPRESS_ENOMEM;
+        }
+        if (w.table) (void)hipFree(w.table);
+        w.table = static_cast<uint64_t*>(p);
+        w.table_cap = cap;
+    }
+    *out = &w;
+    return XPRESS_OK;
+}
+
+template <int T, bool VEC, int COMBINE>
+hipError_t launch_readout(const RowArgs& a, hipStream_t stream)
+{
+    const uint64_t units = (uint64_t)a.rows * a.splits;
+    const uint32_t grid = (uint32_t)(units < (1u << 22) ? units : (1u << 22));
+    hipLaunchKernelGGL((readout_kernel<T, kUnroll, VEC, COMBINE>), dim3(grid), dim3(T), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+template <int T, bool VEC>
+hipError_t launch_by_combine(const RowArgs& a, int combine, hipStream_t stream)
+{
+    switch (combine) {
+        case kSingle: return launch_readout<T, VEC, kSingle>(a, stream);
+        case kAtomic: return launch_readout<T, VEC, kAtomic>(a, stream);
+        default: return launch_readout<T, VEC, kTwoPass>(a, stream);
+    }
+}
+
+template <int T>
+hipError_t launch_by_vec(const RowArgs& a, const Plan& p, hipStream_t stream)
+{
+    return p.vec ? launch_by_combine<T, true>(a, p.combine, stream)
+                 : launch_by_combine<T, false>(a, p.combine, stream);
+}
+
+hipError_t launch_plan(const RowArgs& a, const Plan& p, hipStream_t stream)
+{
+    switch (p.threads) {
+        case 64: return launch_by_vec<64>(a, p, stream);
+        case 128: return launch_by_vec<128>(a, p, stream);
+        case 512: return launch_by_vec<512>(a, p, stream);
+        case 1024: return launch_by_vec<1024>(a, p, stream);
+        default: return launch_by_vec<256>(a, p, stream);
+    }
+}
+
+bool ranges_overlap(const void* p0, size_t n0, const void* p1, size_t n1)
+{
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(p0), a1 = a0 + n0;
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(p1), b1 = b0 + n1;
+    return a0 < b1 && b0 < a1;
+}
+
+int validate(const uint16_t* base, const uint16_t* bias, const int64_t* blk, int64_t N,
+             int64_t B, int64_t V, int64_t sb, int64_t sbi, int64_t* rows_out)
+{
+    if (N < 0 || B < 1 || V < 1 || V > 0x7FFFFFFFll || sb < V || sbi < V) {
+        return XPRESS_EINVAL;
+    }
+    if (B - 1 > 0 && N > INT64_MAX / (B - 1)) return XPRESS_EINVAL;
+    const int64_t rows = N * (B - 1);
+    *rows_out = rows;
+    if (rows == 0) return XPRESS_OK;
+    if (rows > 0x7FFFFFFFll || N > INT64_MAX / B) return XPRESS_EINVAL;
+    if (!base || !bias || !blk) return XPRESS_EINVAL;
+    if ((rows - 1) > (INT64_MAX / 2 - V) / sb || (rows - 1) > (INT64_MAX / 2 - V) / sbi) {
+        return XPRESS_EINVAL;
+    }
+    const size_t base_bytes = (size_t)((rows - 1) * sb + V) * 2u;
+    const size_t bias_bytes = (size_t)((rows - 1) * sbi + V) * 2u;
+    const size_t blk_bytes = (size_t)(N * B) * 8u;
+    if (ranges_overlap(blk, blk_bytes, base, base_bytes) ||
+        ranges_overlap(blk, blk_bytes, bias, bias_bytes)) {
+        return XPRESS_EINVAL;
+    }
+    return XPRESS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int xpress_add_argmax_to_blk(const uint16_t* base, const uint16_t* bias, int64_t* blk,
+                             int64_t N, int64_t B, int64_t V, int64_t stride_base_r,
+                             int64_t stride_bias_r, hipStream_t stream)
+{
+    int64_t rows = 0;
+    int rc = validate(base, bias, blk, N, B, V, stride_base_r, stride_bias_r, &rows);
+    if (rc != XPRESS_OK || rows == 0) return rc;
+
+    const Plan p = make_plan(base, bias, rows, V, stride_base_r, stride_bias_r);
+    RowArgs a;
+    a.base = base;
+    a.bias = bias;
+    a.blk = blk;
+    a.stride_base = stride_base_r;
+    a.stride_bias = stride_bias_r;
+    a.rows = (uint32_t)rows;
+    a.bm1 = (uint32_t)(B - 1);
+    a.V = (uint32_t)V;
+    a.splits = (uint32_t)p.splits;
+    a.keys = nullptr;
+    a.counts = nullptr;
+
+    if (p.combine != kSingle) {
+        Workspace* w = nullptr;
+        const int64_t table = (p.combine == kTwoPass) ? rows * p.splits : 0;
+        rc = ensure_workspace(stream, p.combine == kAtomic ? rows : 0, table, &w);
+        if (rc != XPRESS_OK) return rc;
+        if (p.combine == kAtomic) {
+            a.keys = w->keys;
+            a.counts = w->counts;
+        } else {
+            a.keys = w->table;
+        }
+    }
+
+    hipError_t e = launch_plan(a, p, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    if (p.combine == kTwoPass) {
+        const uint32_t grid = (uint32_t)((rows + 255) / 256 < 65536 ? (rows + 255) / 256 : 65536);
+        hipLaunchKernelGGL(reduce_keys_kernel, dim3(grid), dim3(256), 0, stream, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return XPRESS_OK;
+}
+
+int xpress_reserve(int64_t N, int64_t B, int64_t V, hipStream_t stream)
+{
+    if (N < 0 || B < 1 || V < 1 || V > 0x7FFFFFFFll) return XPRESS_EINVAL;
+    if (B - 1 > 0 && N > 0x7FFFFFFFll / (B - 1)) return XPRESS_EINVAL;
+    const int64_t rows = N * (B - 1);
+    if (rows == 0) return XPRESS_OK;
+    // reserve for both the aligned and the unaligned plan of this shape
+    const uint16_t* aligned = reinterpret_cast<const uint16_t*>(uintptr_t(256));
+    const Plan pv = make_plan(aligned, aligned, rows, V, (V + 7) / 8 * 8, (V + 7) / 8 * 8);
+    const Plan ps = make_plan(aligned + 1, aligned + 1, rows, V, V | 1, V | 1);
+    int64_t table = 0;
+    if (pv.combine == kTwoPass) table = rows * pv.splits;
+    if (ps.combine == kTwoPass && rows * ps.splits > table) table = rows * ps.splits;
+    Workspace* w = nullptr;
+    return ensure_workspace(stream, rows, table, &w);
+}
+
+int xpress_release(void)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e);
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    for (auto it = g_ws.begin(); it != g_ws.end();) {
+        if (it->first.first == dev) {
+            if (it->second.keys) (void)hipFree(it->second.keys);
+            if (it->second.table) (void)hipFree(it->second.table);
+            it = g_ws.erase(it);
+        } else {
+            ++it;
+        }
+    }
+    return XPRESS_OK;
+}
+
+int xpress_set_plan(int combine, int splits, int block_threads)
+{
+    if (combine < XPRESS_COMBINE_AUTO || combine > XPRESS_COMBINE_TWO_PASS) return XPRESS_EINVAL;
+    if (splits < 0) return XPRESS_EINVAL;
+    if (block_threads != 0 && block_threads != 64 && block_threads != 128 &&
+        block_threads != 256 && block_threads != 512 && block_threads != 1024) {
+        return XPRESS_EINVAL;
+    }
+    std::lock_guard<std::mutex> lk(g_plan_mu);
+    g_override_combine = combine;
+    g_override_splits = splits;
+    g_override_threads = block_threads;
+    return XPRESS_OK;
+}
+
+int xpress_describe_plan(const uint16_t* base, const uint16_t* bias, int64_t N, int64_t B,
+                         int64_t V, int64_t stride_base_r, int64_t stride_bias_r,
+                         int* combine, int* splits, int* block_threads, int* vector_path,
+                         int* launches)
+{
+    if (N < 0 || B < 1 || V < 1 || V > 0x7FFFFFFFll || stride_base_r < V ||
+        stride_bias_r < V) {
+        return XPRESS_EINVAL;
+    }
+    const int64_t rows = N * (B - 1);
+    const Plan p = make_plan(base, bias, rows > 0 ? rows : 1, V, stride_base_r, stride_bias_r);
+    if (combine) *combine = p.combine;
+    if (splits) *splits = p.splits;
+    if (block_threads) *block_threads = p.threads;
+    if (vector_path) *vector_path = p.vec ? 1 : 0;
+    if (launches) *launches = rows > 0 ? p.launches : 0;
+    return XPRESS_OK;
+}
+
+int xpress_bf16_add_round_table(const uint16_t* a_vals, int64_t n_a, uint16_t* out,
+                                hipStream_t stream)
+{
+    if (n_a < 0 || n_a > 65536) return XPRESS_EINVAL;
+    if (n_a == 0) return XPRESS_OK;
+    if (!a_vals || !out || (reinterpret_cast<uintptr_t>(out) & 3u)) return XPRESS_EINVAL;
+    const uint64_t total = (uint64_t)n_a * 32768u;
+    const uint64_t blocks = (total + 255) / 256;
+    const uint32_t grid = (uint32_t)(blocks < 65536 ? blocks : 65536);
+    hipLaunchKernelGGL(round_table_kernel, dim3(grid), dim3(256), 0, stream, a_vals,
+                       (uint32_t)n_a, reinterpret_cast<uint32_t*>(out));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e);
+    return XPRESS_OK;
+}
+
+int xpress_last_hip_error(void) { return g_last_hip_error; }
+
+const char* xpress_error_string(int status)
+{
+    switch (status) {
+        case XPRESS_OK: return "ok";
+        case XPRESS_EINVAL: return "invalid argument: the sizes, strides or pointers describe no valid layout";
+        case XPRESS_EHIP: return "a HIP call failed (see xpress_last_hip_error)";
+        case XPRESS_ENOMEM: return "could not allocate the device workspace";
+        case XPRESS_ECAPTURE: return "the workspace must grow while the stream is capturing; call xpress_reserve first";
+        default: return "unknown status";
+    }
+}
+
+const char* xpress_version(void) { return "0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,164 @@
+"""ctypes binding of ``libxpress_argmax.so`` (declared in include/xpress_argmax.h).
+
+Argument marshalling only: every step of the readout runs in the library's
+HIP kernels.  Entry points keep the C names.  Tensor arguments may be torch
+tensors on a GPU (their ``data_ptr()`` is passed) or plain integer device
+addresses.  A nonzero status raises :class:`XpressError`.  If the library has
+not been built, the first call raises -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libxpress_argmax.so")
+
+XPRESS_OK = 0
+XPRESS_EINVAL = 1
+XPRESS_EHIP = 2
+XPRESS_ENOMEM = 3
+XPRESS_ECAPTURE = 4
+
+XPRESS_COMBINE_AUTO = 0
+XPRESS_COMBINE_SINGLE = 1
+XPRESS_COMBINE_ATOMIC = 2
+XPRESS_COMBINE_TWO_PASS = 3
+
+COMBINE_NAMES = {XPRESS_COMBINE_SINGLE: "single", XPRESS_COMBINE_ATOMIC: "atomic",
+                 XPRESS_COMBINE_TWO_PASS: "two_pass"}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class XpressError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = "%s: %s" % (where, xpress_error_string(status))
+        if status == XPRESS_EHIP:
+            msg += " (hipError %d)" % xpress_last_hip_error()
+        super().__init__(msg)
+
+
+def load():
+    """Load the library (once).  Raises ImportError when it is not built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                "libxpress_argmax.so is not built; run `python -m vocab_wide_add_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        ip = ctypes.POINTER(ctypes.c_int)
+        lib.xpress_add_argmax_to_blk.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, vp]
+        lib.xpress_add_argmax_to_blk.restype = i32
+        lib.xpress_reserve.argtypes = [i64, i64, i64, vp]
+        lib.xpress_reserve.restype = i32
+        lib.xpress_release.argtypes = []
+        lib.xpress_release.restype = i32
+        lib.xpress_set_plan.argtypes = [i32, i32, i32]
+        lib.xpress_set_plan.restype = i32
+        lib.xpress_describe_plan.argtypes = [vp, vp, i64, i64, i64, i64, i64,
+                                             ip, ip, ip, ip, ip]
+        lib.xpress_describe_plan.restype = i32
+        lib.xpress_bf16_add_round_table.argtypes = [vp, i64, vp, vp]
+        lib.xpress_bf16_add_round_table.restype = i32
+        lib.xpress_last_hip_error.argtypes = []
+        lib.xpress_last_hip_error.restype = i32
+        lib.xpress_error_string.argtypes = [i32]
+        lib.xpress_error_string.restype = ctypes.c_char_p
+        lib.xpress_version.argtypes = []
+        lib.xpress_version.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def _ptr(x):
+    """Device address of a torch tensor on a GPU, or an int address as is."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        if not x.is_cuda:
+            raise ValueError("expected a tensor on a GPU, got one on %s" % x.device)
+        return x.data_ptr()
+    raise TypeError("expected a GPU tensor or an integer address, got %r" % type(x))
+
+
+def _stream(stream):
+    """HIP stream handle: None means torch's current stream on the current device."""
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != XPRESS_OK:
+        raise XpressError(status, where)
+
+
+def xpress_add_argmax_to_blk(base, bias, blk, N: int, B: int, V: int,
+                             stride_base_r: int, stride_bias_r: int, stream=None) -> None:
+    """blk[n, 1+b] = argmax_v bf16(base[r, v] + bias[r, v]), r = n*(B-1) + b.
+
+    Queued on ``stream`` (default: torch's current stream).  See the header
+    for the layout rules and error behaviour.
+    """
+    lib = load()
+    _check(lib.xpress_add_argmax_to_blk(_ptr(base), _ptr(bias), _ptr(blk), int(N), int(B),
+                                        int(V), int(stride_base_r), int(stride_bias_r),
+                                        _stream(stream)),
+           "xpress_add_argmax_to_blk")
+
+
+def xpress_reserve(N: int, B: int, V: int, stream=None) -> None:
+    _check(load().xpress_reserve(int(N), int(B), int(V), _stream(stream)), "xpress_reserve")
+
+
+def xpress_release() -> None:
+    _check(load().xpress_release(), "xpress_release")
+
+
+def xpress_set_plan(combine: int = XPRESS_COMBINE_AUTO, splits: int = 0,
+                    block_threads: int = 0) -> None:
+    _check(load().xpress_set_plan(int(combine), int(splits), int(block_threads)),
+           "xpress_set_plan")
+
+
+def xpress_describe_plan(base, bias, N: int, B: int, V: int, stride_base_r: int,
+                         stride_bias_r: int) -> dict:
+    """The plan a call would use, from sizes and pointer alignment (host only)."""
+    out = [ctypes.c_int(0) for _ in range(5)]
+    _check(load().xpress_describe_plan(
+        _ptr(base), _ptr(bias), int(N), int(B), int(V), int(stride_base_r),
+        int(stride_bias_r), *[ctypes.byref(o) for o in out]), "xpress_describe_plan")
+    combine, splits, threads, vec, launches = [o.value for o in out]
+    return {"combine": COMBINE_NAMES.get(combine, combine), "splits": splits,
+            "block_threads": threads, "vector_path": bool(vec), "launches": launches}
+
+
+def xpress_bf16_add_round_table(a_vals, n_a: int, out, stream=None) -> None:
+    """out[i*65536 + b] = bf16(a_vals[i] + b) on the GPU, for every pattern b."""
+    _check(load().xpress_bf16_add_round_table(_ptr(a_vals), int(n_a), _ptr(out),
+                                              _stream(stream)),
+           "xpress_bf16_add_round_table")
+
+
+def xpress_last_hip_error() -> int:
+    return int(load().xpress_last_hip_error())
+
+
+def xpress_error_string(status: int) -> str:
+    return load().xpress_error_string(int(status)).decode()
+
+
+def xpress_version() -> str:
+    return load().xpress_version().decode()
