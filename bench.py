@@ -175,7 +175,7 @@ def main():
     achieved = bytes_per_call / kavg / 1e9
     traffic = traffic_for(name)
     out = {
-        "metric": "effective HBM GB/s (+ % of peak) and rows/s, add+argmax N=%d B=%d V=%d"
+        "metric": "effective HBM GB/s (+ %% of peak) and rows/s, add+argmax N=%d B=%d V=%d"
                   % (w.N, w.B, w.V),
         "value": round(value, 1),
         "unit": "GB/s",
