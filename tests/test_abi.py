@@ -39,8 +39,16 @@ def test_version_and_strings():
 
 
 def test_plan_for_the_pages_shape():
+    # measured default: one 1024-thread workgroup per row at 480 rows
     p = native.xpress_describe_plan(256, 256, 32, 16, 152064, 152064, 152064)
-    assert p["vector_path"] and p["launches"] == 1 and p["splits"] >= 2
+    assert p["vector_path"] and p["launches"] == 1
+    assert (p["combine"], p["splits"], p["block_threads"]) == ("single", 1, 1024)
+    # a few very wide rows are split and combined in a second pass
+    p = native.xpress_describe_plan(256, 256, 1, 9, 152064, 152064, 152064)
+    assert (p["combine"], p["launches"]) == ("two_pass", 2) and p["splits"] >= 2
+    # short rows get a smaller workgroup
+    p = native.xpress_describe_plan(256, 256, 2, 4, 1000, 1000, 1000)
+    assert p["block_threads"] == 64
     p = native.xpress_describe_plan(258, 256, 32, 16, 152064, 152064, 152064)
     assert not p["vector_path"]
     p = native.xpress_describe_plan(256, 256, 32, 16, 152064, 152065, 152064)

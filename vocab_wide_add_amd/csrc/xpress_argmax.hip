@@ -415,9 +415,27 @@ int g_override_combine = XPRESS_COMBINE_AUTO;
 int g_override_splits = 0;
 int g_override_threads = 0;
 
-constexpr int kUnroll = 4;
+// Vectors of each stream in flight per thread before the first use.  Measured
+// at 480 x 152064 on MI355X: 2 and 3 within noise of each other, 1 and 4-8
+// slower at 1024 threads.
+constexpr int kUnroll = 2;
+
+// Below this many rows the default plan splits rows over workgroups, aiming
+// at about kSplitTargetUnits workgroups in all.
+constexpr int64_t kSplitBelowRows = 128;
+constexpr int64_t kSplitTargetUnits = 512;
 
 bool is_aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Largest workgroup size that still gives every thread at least two unrolled
+// rounds of loads in a row of V elements.
+int auto_threads(int64_t V, bool vec)
+{
+    const int64_t units = vec ? V / 8 : V;
+    int t = 1024;
+    while (t > 64 && units < (int64_t)t * kUnroll * 2) t /= 2;
+    return t;
+}
 
 Plan make_plan(const uint16_t* base, const uint16_t* bias, int64_t rows, int64_t V,
                int64_t sb, int64_t sbi)
@@ -431,29 +449,39 @@ Plan make_plan(const uint16_t* base, const uint16_t* bias, int64_t rows, int64_t
         os = g_override_splits;
         ot = g_override_threads;
     }
-    p.threads = ot ? ot : 256;
-    // Units of work a row can be cut into without starving a workgroup:
-    // at least two unrolled rounds of loads per thread.
-    const int64_t per_unit = (int64_t)p.threads * kUnroll * 2 * (p.vec ? 8 : 1);
-    int64_t max_splits = V / per_unit;
+    p.threads = ot ? ot : auto_threads(V, p.vec);
+    // Measured on MI355X: one workgroup per row streams at the same rate as
+    // a plain read kernel once there are a few hundred rows, and stays the
+    // fastest down to tens of rows (the second launch of the two-pass
+    // combine costs ~2 us; the atomic combine's release fence costs ~40 ns
+    // per workgroup, serialised).  Only a handful of very wide rows leave
+    // most CUs idle; those are split and combined in two passes.
+    const int64_t per_split = (int64_t)p.threads * kUnroll * 2 * (p.vec ? 8 : 1);
+    int64_t max_splits = V / per_split;
     if (max_splits < 1) max_splits = 1;
-    // Aim for about 16 workgroups per CU over 256 CUs.
-    const int64_t target_units = 4096;
-    int64_t s = (target_units + rows - 1) / rows;
-    if (s > max_splits) s = max_splits;
-    if (s < 1) s = 1;
-    if (os > 0) s = os;
+    int64_t s = 1;
+    int combine = kSingle;
+    if (rows < kSplitBelowRows && max_splits > 1) {
+        s = (kSplitTargetUnits + rows - 1) / rows;
+        if (s > max_splits) s = max_splits;
+        if (s > 1) combine = kTwoPass;
+        else s = 1;
+    }
+    if (oc != XPRESS_COMBINE_AUTO) {
+        combine = oc;
+        if (os > 0) s = os;
+        else if (combine != kSingle && s == 1) s = max_splits < 8 ? max_splits : 8;
+    } else if (os > 0) {
+        s = os;
+        if (s > 1 && combine == kSingle) combine = kTwoPass;
+    }
     if (s > 65535) s = 65535;
     // (row, split) units are counted in 32 bits on the device
     if (s > 1 && rows * s > 0x7FFFFFFFll) s = 0x7FFFFFFFll / rows;
     if (s < 1) s = 1;
+    if (combine == kSingle) s = 1;
+    p.combine = combine;
     p.splits = (int)s;
-    if (oc == XPRESS_COMBINE_AUTO) {
-        p.combine = (p.splits == 1) ? kSingle : kAtomic;
-    } else {
-        p.combine = oc;
-    }
-    if (p.combine == kSingle) p.splits = 1;
     p.launches = (p.combine == kTwoPass) ? 2 : 1;
     return p;
 }
