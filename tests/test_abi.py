@@ -39,10 +39,13 @@ def test_version_and_strings():
 
 
 def test_plan_for_the_pages_shape():
-    # measured default: one 1024-thread workgroup per row at 480 rows
+    # measured default: one 256-thread workgroup per row at 480 rows
     p = native.xpress_describe_plan(256, 256, 32, 16, 152064, 152064, 152064)
     assert p["vector_path"] and p["launches"] == 1
-    assert (p["combine"], p["splits"], p["block_threads"]) == ("single", 1, 1024)
+    assert (p["combine"], p["splits"], p["block_threads"]) == ("single", 1, 256)
+    # 1024 threads per row from 1024 rows on
+    p = native.xpress_describe_plan(256, 256, 256, 16, 152064, 152064, 152064)
+    assert (p["combine"], p["block_threads"]) == ("single", 1024)
     # a few very wide rows are split and combined in a second pass
     p = native.xpress_describe_plan(256, 256, 1, 9, 152064, 152064, 152064)
     assert (p["combine"], p["launches"]) == ("two_pass", 2) and p["splits"] >= 2

@@ -427,12 +427,15 @@ constexpr int64_t kSplitTargetUnits = 512;
 
 bool is_aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Largest workgroup size that still gives every thread at least two unrolled
-// rounds of loads in a row of V elements.
-int auto_threads(int64_t V, bool vec)
+// Workgroup size of the default plan.  Measured on MI355X with one
+// workgroup per row (interleaved medians): at 480 rows x 152064, 256 threads
+// 44.8 us vs 45.5 us for 512 or 1024; at 3840 rows, 1024 threads ~2% ahead
+// of 256; below 128 rows (split plans) 1024.  Capped so that every thread
+// still gets at least two unrolled rounds of loads in a row of V elements.
+int auto_threads(int64_t rows, int64_t V, bool vec)
 {
     const int64_t units = vec ? V / 8 : V;
-    int t = 1024;
+    int t = (rows >= kSplitBelowRows && rows < 1024) ? 256 : 1024;
     while (t > 64 && units < (int64_t)t * kUnroll * 2) t /= 2;
     return t;
 }
@@ -449,7 +452,7 @@ Plan make_plan(const uint16_t* base, const uint16_t* bias, int64_t rows, int64_t
         os = g_override_splits;
         ot = g_override_threads;
     }
-    p.threads = ot ? ot : auto_threads(V, p.vec);
+    p.threads = ot ? ot : auto_threads(rows, V, p.vec);
     // Measured on MI355X: one workgroup per row streams at the same rate as
     // a plain read kernel once there are a few hundred rows, and stays the
     // fastest down to tens of rows (the second launch of the two-pass
