@@ -73,7 +73,8 @@ extern "C" {
  * next synchronisation, as for any HIP kernel.
  *
  * Workspace: when the chosen plan splits a row over several workgroups the
- * library uses a small device workspace of its own (about 12 bytes per row),
+ * library uses a small device workspace of its own (8 bytes per row, or per
+ * row and split for the two-pass plan),
  * one per (device, stream), allocated on first use and left zeroed by every
  * call, so repeated calls and graph replays need no clearing.  Calls queued
  * on different streams use different workspaces and may run concurrently.
@@ -104,22 +105,31 @@ int xpress_release(void);
  * results meet:
  *   XPRESS_COMBINE_AUTO    the library's measured choice per shape;
  *   XPRESS_COMBINE_SINGLE  one workgroup per row, no cross-workgroup step;
- *   XPRESS_COMBINE_ATOMIC  several workgroups per row; each folds a packed
- *                          64-bit (value, ~index) key into the row's slot with
- *                          an atomic max, and the last to arrive writes blk
- *                          and clears the slot (one launch);
+ *   XPRESS_COMBINE_ATOMIC  several workgroups per row; each folds its packed
+ *                          (value, ~index) key into a per-row 64-bit word that
+ *                          also counts arrivals, by compare-and-swap; the last
+ *                          to arrive writes blk and clears the word (one
+ *                          launch);
  *   XPRESS_COMBINE_TWO_PASS several workgroups per row write their packed key
  *                          to a [rows, splits] table, a second small kernel
- *                          reduces each row (two launches).
+ *                          reduces each row (two launches);
+ *   XPRESS_COMBINE_BALANCED the rows' 16-byte vectors, in row-major order, are
+ *                          cut into equal contiguous ranges, one per
+ *                          workgroup, over a whole number of workgroups per
+ *                          CU; rows shared by several ranges are folded as in
+ *                          ATOMIC (one launch; needs the aligned layout and
+ *                          V >= 8, else it falls back to SINGLE).
  * splits is the number of workgroups per row (0 = automatic; ignored by
- * SINGLE).  block_threads is the workgroup size (0 = automatic, else 64,
- * 128, 256, 512 or 1024).  The setting is process-wide and applies to later
- * calls.  Returns XPRESS_EINVAL for an unknown combine or block size.
+ * SINGLE); for BALANCED it is the number of workgroups per CU.  block_threads
+ * is the workgroup size (0 = automatic, else 64, 128, 256, 512 or 1024).  The
+ * setting is process-wide and applies to later calls.  Returns XPRESS_EINVAL
+ * for an unknown combine or block size.
  */
 #define XPRESS_COMBINE_AUTO 0
 #define XPRESS_COMBINE_SINGLE 1
 #define XPRESS_COMBINE_ATOMIC 2
 #define XPRESS_COMBINE_TWO_PASS 3
+#define XPRESS_COMBINE_BALANCED 4
 int xpress_set_plan(int combine, int splits, int block_threads);
 
 /*

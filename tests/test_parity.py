@@ -19,7 +19,7 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
 COMBINES = [native.XPRESS_COMBINE_SINGLE, native.XPRESS_COMBINE_ATOMIC,
-            native.XPRESS_COMBINE_TWO_PASS]
+            native.XPRESS_COMBINE_TWO_PASS, native.XPRESS_COMBINE_BALANCED]
 
 _cache = {}
 
@@ -260,7 +260,8 @@ def test_signed_zero_and_special_rows(combine):
 
 
 @pytest.mark.parametrize("combine", [native.XPRESS_COMBINE_ATOMIC,
-                                     native.XPRESS_COMBINE_TWO_PASS])
+                                     native.XPRESS_COMBINE_TWO_PASS,
+                                     native.XPRESS_COMBINE_BALANCED])
 def test_repeated_calls_leave_a_clean_workspace(combine):
     import torch
     N, B, V = 6, 9, 30000
@@ -357,3 +358,50 @@ def test_element_step_every_bf16_pair():
         assert np.array_equal(nan_g, nan_w), s
         bad += int(np.count_nonzero((got != want) & ~nan_w))
     assert bad == 0
+
+
+def _balanced_edges(rows, V, per_cu):
+    """Range boundaries (row, vector) of the balanced plan for these sizes."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    g = cus * per_cu
+    nvec = V // 8
+    q = rows * nvec
+    edges = sorted({(k * q) // g for k in range(1, g)})
+    return [(x // nvec, x % nvec) for x in edges]
+
+
+@pytest.mark.parametrize("per_cu,threads", [(1, 256), (2, 256), (3, 128), (2, 1024)])
+def test_balanced_ties_on_range_edges(per_cu, threads):
+    """Equal maxima placed on both sides of the balanced plan's range edges
+    (the last vector of one workgroup's range and the first of the next):
+    the lower index must win, and rows shared by 2-3 ranges must fold to the
+    same answer as the oracle."""
+    rows, V = 300, 9000 + 5   # V % 8 != 0: the tail follows the row's last vector
+    S = V + 3                 # row stride a multiple of 8 elements (16-byte rows)
+    g = np.random.Generator(np.random.PCG64(per_cu * 7 + threads))
+    base = np.full((rows, S), 0x42C8, dtype=np.uint16)   # +100 poison in the padding
+    bias = np.zeros((rows, S), dtype=np.uint16)
+    base[:, :V] = 0x3F80                                  # 1.0
+    for r, qv in _balanced_edges(rows, V, per_cu):
+        e = qv * 8
+        base[r, e] = 0x4000                 # 2.0 at the first element of the range
+        if e >= 1:
+            base[r, e - 1] = 0x4000         # and at the last element of the previous one
+    # some rows: maximum only in the tail, or a single copy anywhere
+    for r in range(0, rows, 17):
+        base[r, V - 1] = 0x4040
+    for r in range(5, rows, 23):
+        base[r, :V] = 0x3F80
+        base[r, int(g.integers(0, V))] = 0x4000
+    N, B = rows, 2
+    blk0 = np.full((N, B), 11, dtype=np.int64)
+    want = oracle_blk(base, bias, blk0, N, B, V, S, S)
+    bd, id_ = to_dev(base), to_dev(bias)
+    with Plan(native.XPRESS_COMBINE_BALANCED, per_cu, threads):
+        plan = native.xpress_describe_plan(bd, id_, N, B, V, S, S)
+        assert plan["combine"] == "balanced", plan
+        say("balanced range edges per_cu=%d threads=%d" % (per_cu, threads))
+        for _ in range(3):
+            got = gpu_blk(bd, id_, blk0, N, B, V, S, S)
+            assert np.array_equal(got, want)

@@ -153,10 +153,11 @@ __device__ __forceinline__ void block_argmax(float& v, uint32_t& i)
     }
 }
 
-// Packed order-preserving key: (ordered bf16 of the value) << 32 | ~index.
-// Unsigned order of keys == (value desc, index asc) order of candidates.
-// -0 is mapped to +0 first so the two compare equal.  A missing candidate
-// is the key 0, below every real key (real keys have ~index >= 2^31).
+// Packed order-preserving 48-bit key: (ordered bf16 of the value) << 32 |
+// ~index.  Unsigned order of keys == (value desc, index asc) order of
+// candidates.  -0 is mapped to +0 first so the two compare equal.  A missing
+// candidate is the key 0, below every real key (real keys have ~index >=
+// 2^31).
 __device__ __forceinline__ uint64_t make_key(float v, uint32_t i)
 {
     if (i == kNoIndex) {
@@ -282,18 +283,43 @@ struct RowArgs {
     uint32_t bm1;         // B - 1
     uint32_t V;
     uint32_t splits;      // workgroups per row
-    uint64_t* keys;       // ATOMIC: [rows] keys; TWO_PASS: [rows, splits] table
-    uint32_t* counts;     // ATOMIC: [rows] arrival counts
+    uint64_t* keys;       // ATOMIC: [rows] key-and-count words;
+                          // TWO_PASS: [rows, splits] key table
 };
 
 enum Combine { kSingle = XPRESS_COMBINE_SINGLE, kAtomic = XPRESS_COMBINE_ATOMIC,
-               kTwoPass = XPRESS_COMBINE_TWO_PASS };
+               kTwoPass = XPRESS_COMBINE_TWO_PASS, kBalanced = XPRESS_COMBINE_BALANCED };
 
 __device__ __forceinline__ void write_blk(const RowArgs& a, uint32_t row, int64_t idx)
 {
     const uint32_t n = row / a.bm1;
     const uint32_t b = row - n * a.bm1;
     a.blk[(int64_t)n * (a.bm1 + 1) + 1 + b] = idx;
+}
+
+// Fold one workgroup's candidate key into its row's 64-bit word, which holds
+// (best key so far) << 16 | the number of workgroups that have folded in.
+// Every access to the word is an atomic operation on that one location, so
+// the updates are totally ordered and each compare-and-swap sees every
+// earlier one: the workgroup that finds the count at arrivals - 1 holds the
+// row's final key in its own new value.  It writes blk and clears the word
+// for the next call.  No fence is needed: nothing else is published between
+// workgroups.  arrivals <= 65535.
+__device__ __forceinline__ void fold_key(const RowArgs& a, uint32_t row, uint64_t key,
+                                         uint32_t arrivals)
+{
+    uint64_t* word = &a.keys[row];
+    uint64_t old = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint64_t desired;
+    do {
+        const uint64_t best = old >> 16;
+        desired = ((key > best ? key : best) << 16) | ((old + 1u) & 0xFFFFu);
+    } while (!__hip_atomic_compare_exchange_weak(word, &old, desired, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if ((old & 0xFFFFu) == arrivals - 1u) {
+        __hip_atomic_store(word, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        write_blk(a, row, key_index(desired >> 16));
+    }
 }
 
 // One workgroup per (row, split) unit; the grid strides over units so any
@@ -336,25 +362,67 @@ __global__ __launch_bounds__(T) void readout_kernel(RowArgs a)
             } else if constexpr (COMBINE == kTwoPass) {
                 a.keys[(uint64_t)row * a.splits + split] = make_key(v, i);
             } else {
-                const uint64_t key = make_key(v, i);
-                if (key != 0) {
-                    __hip_atomic_fetch_max(&a.keys[row], key, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-                }
-                // release: this workgroup's key is in before its arrival
-                // counts; acquire: the last arriver sees every key.
-                const uint32_t prev = __hip_atomic_fetch_add(
-                    &a.counts[row], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-                if (prev == a.splits - 1) {
-                    const uint64_t k = __hip_atomic_exchange(
-                        &a.keys[row], (uint64_t)0, __ATOMIC_RELAXED,
-                        __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(&a.counts[row], 0u, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                    write_blk(a, row, key_index(k));
-                }
+                fold_key(a, row, make_key(v, i), a.splits);
             }
         }
+    }
+}
+
+// Balanced plan: the full 16-byte vectors of all rows, in row-major order,
+// are cut into gridDim.x equal contiguous ranges, one per workgroup, with the
+// grid sized to a whole number of workgroups per CU.  Every CU then streams
+// the same number of bytes, so none idles while others finish (one workgroup
+// per row leaves the CUs that received fewer rows idle at the end).  A
+// workgroup meets each row its range touches; a row wholly inside one range
+// is written directly, a row shared by several ranges is folded through its
+// key-and-count word, expecting as many arrivals as ranges touch it.
+// Requires V >= 8, 16-byte aligned rows, and at least one vector per range.
+__device__ __forceinline__ uint32_t range_of(uint64_t x, uint64_t q, uint64_t g)
+{
+    // the range [floor(k*q/g), floor((k+1)*q/g)) that holds vector x
+    return (uint32_t)(((x + 1u) * g - 1u) / q);
+}
+
+template <int T, int UNROLL>
+__global__ __launch_bounds__(T) void readout_balanced_kernel(RowArgs a)
+{
+    const uint64_t nvec = a.V / 8u;
+    const uint64_t q = (uint64_t)a.rows * nvec;
+    const uint64_t g = gridDim.x;
+    const uint64_t x1 = ((uint64_t)blockIdx.x + 1u) * q / g;
+    uint64_t x = (uint64_t)blockIdx.x * q / g;
+    while (x < x1) {
+        const uint32_t row = (uint32_t)(x / nvec);
+        const uint64_t row0 = (uint64_t)row * nvec;
+        const uint64_t seg_end = (x1 < row0 + nvec) ? x1 : row0 + nvec;
+        const uint32_t q0 = (uint32_t)(x - row0);
+        const uint32_t q1 = (uint32_t)(seg_end - row0);
+        const uint16_t* rb = a.base + (int64_t)row * a.stride_base;
+        const uint16_t* ri = a.bias + (int64_t)row * a.stride_bias;
+
+        float v;
+        uint32_t i;
+        scan_vectors<T, UNROLL>(reinterpret_cast<const u32x4*>(rb),
+                                reinterpret_cast<const u32x4*>(ri), q0, q1, v, i);
+        // the last V % 8 elements go with the row's last vector
+        const uint32_t tail0 = (uint32_t)nvec * 8u;
+        if (q1 == (uint32_t)nvec && tail0 + threadIdx.x < a.V) {
+            const uint32_t e = tail0 + threadIdx.x;
+            merge(v, i, add_round1(rb[e], ri[e]), e);
+        }
+
+        block_argmax<T>(v, i);
+
+        if (threadIdx.x == 0) {
+            const uint32_t first = range_of(row0, q, g);
+            const uint32_t last = range_of(row0 + nvec - 1u, q, g);
+            if (first == last) {
+                write_blk(a, row, (int64_t)i);
+            } else {
+                fold_key(a, row, make_key(v, i), last - first + 1u);
+            }
+        }
+        x = seg_end;
     }
 }
 
@@ -404,11 +472,28 @@ int hip_fail(hipError_t e)
 
 struct Plan {
     int combine;
-    int splits;
+    int splits;   // workgroups per row; for kBalanced, workgroups per CU
     int threads;
     bool vec;
     int launches;
+    uint32_t grid;  // kBalanced: total workgroups
 };
+
+// Compute units of the current device, cached per device.
+int device_cus()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0) {
+        n = 256;
+    }
+    if (dev < 64) cached[dev] = n;
+    return n;
+}
 
 std::mutex g_plan_mu;
 int g_override_combine = XPRESS_COMBINE_AUTO;
@@ -424,6 +509,9 @@ constexpr int kUnroll = 2;
 // at about kSplitTargetUnits workgroups in all.
 constexpr int64_t kSplitBelowRows = 128;
 constexpr int64_t kSplitTargetUnits = 512;
+
+// Workgroups per CU of the balanced plan.
+constexpr int64_t kBalancedPerCu = 2;
 
 bool is_aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -483,19 +571,34 @@ Plan make_plan(const uint16_t* base, const uint16_t* bias, int64_t rows, int64_t
     if (s > 1 && rows * s > 0x7FFFFFFFll) s = 0x7FFFFFFFll / rows;
     if (s < 1) s = 1;
     if (combine == kSingle) s = 1;
+    p.grid = 0;
+    if (combine == kBalanced) {
+        // s = workgroups per CU; every range must hold at least one vector,
+        // and the range arithmetic stays in 64 bits
+        const int64_t per_cu = (os > 0) ? os : kBalancedPerCu;
+        const int64_t g = (int64_t)device_cus() * (per_cu < 1 ? 1 : (per_cu > 64 ? 64 : per_cu));
+        const int64_t q = rows * (V / 8);
+        // (x + 1) * g must not overflow 64 bits for x < q
+        if (!p.vec || V < 8 || q < g || q > ((int64_t)1 << 62) / g) {
+            combine = kSingle;
+            s = 1;
+        } else {
+            s = g / device_cus();
+            p.grid = (uint32_t)g;
+        }
+    }
     p.combine = combine;
     p.splits = (int)s;
     p.launches = (p.combine == kTwoPass) ? 2 : 1;
     return p;
 }
 
-// Per (device, stream) workspace.  The atomic region ([rows] u64 keys and
-// [rows] u32 counts) is zero when idle: allocated zeroed, and every call's
-// last arriver clears what it used.  The table region is overwritten whole
-// by every two-pass call.
+// Per (device, stream) workspace.  The atomic region ([rows] u64
+// key-and-count words) is zero when idle: allocated zeroed, and every call's
+// last arriver clears the word it used.  The table region is overwritten
+// whole by every two-pass call.
 struct Workspace {
     uint64_t* keys = nullptr;
-    uint32_t* counts = nullptr;
     int64_t rows_cap = 0;
     uint64_t* table = nullptr;
     int64_t table_cap = 0;
@@ -536,12 +639,12 @@ int ensure_workspace(hipStream_t stream, int64_t rows, int64_t table, Workspace*
     if (grow_rows) {
         int64_t cap = rows < 4096 ? 4096 : rows;
         void* p = nullptr;
-        e = hipMalloc(&p, (size_t)cap * 12u);
+        e = hipMalloc(&p, (size_t)cap * 8u);
         if (e != hipSuccess) {
             g_last_hip_error = (int)e;
             return XPRESS_ENOMEM;
         }
-        e = hipMemset(p, 0, (size_t)cap * 12u);
+        e = hipMemset(p, 0, (size_t)cap * 8u);
         if (e != hipSuccess) {
             (void)hipFree(p);
             return hip_fail(e);
@@ -553,7 +656,6 @@ int ensure_workspace(hipStream_t stream, int64_t rows, int64_t table, Workspace*
         }
         if (w.keys) (void)hipFree(w.keys);
         w.keys = static_cast<uint64_t*>(p);
-        w.counts = reinterpret_cast<uint32_t*>(static_cast<char*>(p) + (size_t)cap * 8u);
         w.rows_cap = cap;
     }
     if (grow_table) {
@@ -599,8 +701,25 @@ hipError_t launch_by_vec(const RowArgs& a, const Plan& p, hipStream_t stream)
                  : launch_by_combine<T, false>(a, p.combine, stream);
 }
 
+template <int T>
+hipError_t launch_balanced(const RowArgs& a, const Plan& p, hipStream_t stream)
+{
+    hipLaunchKernelGGL((readout_balanced_kernel<T, kUnroll>), dim3(p.grid), dim3(T), 0, stream,
+                       a);
+    return hipGetLastError();
+}
+
 hipError_t launch_plan(const RowArgs& a, const Plan& p, hipStream_t stream)
 {
+    if (p.combine == kBalanced) {
+        switch (p.threads) {
+            case 64: return launch_balanced<64>(a, p, stream);
+            case 128: return launch_balanced<128>(a, p, stream);
+            case 512: return launch_balanced<512>(a, p, stream);
+            case 1024: return launch_balanced<1024>(a, p, stream);
+            default: return launch_balanced<256>(a, p, stream);
+        }
+    }
     switch (p.threads) {
         case 64: return launch_by_vec<64>(a, p, stream);
         case 128: return launch_by_vec<128>(a, p, stream);
@@ -666,16 +785,15 @@ int xpress_add_argmax_to_blk(const uint16_t* base, const uint16_t* bias, int64_t
     a.V = (uint32_t)V;
     a.splits = (uint32_t)p.splits;
     a.keys = nullptr;
-    a.counts = nullptr;
 
     if (p.combine != kSingle) {
         Workspace* w = nullptr;
         const int64_t table = (p.combine == kTwoPass) ? rows * p.splits : 0;
-        rc = ensure_workspace(stream, p.combine == kAtomic ? rows : 0, table, &w);
+        const bool words = (p.combine == kAtomic || p.combine == kBalanced);
+        rc = ensure_workspace(stream, words ? rows : 0, table, &w);
         if (rc != XPRESS_OK) return rc;
-        if (p.combine == kAtomic) {
+        if (words) {
             a.keys = w->keys;
-            a.counts = w->counts;
         } else {
             a.keys = w->table;
         }
@@ -731,7 +849,7 @@ int xpress_release(void)
 
 int xpress_set_plan(int combine, int splits, int block_threads)
 {
-    if (combine < XPRESS_COMBINE_AUTO || combine > XPRESS_COMBINE_TWO_PASS) return XPRESS_EINVAL;
+    if (combine < XPRESS_COMBINE_AUTO || combine > XPRESS_COMBINE_BALANCED) return XPRESS_EINVAL;
     if (splits < 0) return XPRESS_EINVAL;
     if (block_threads != 0 && block_threads != 64 && block_threads != 128 &&
         block_threads != 256 && block_threads != 512 && block_threads != 1024) {

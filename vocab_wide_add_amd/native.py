@@ -25,9 +25,10 @@ XPRESS_COMBINE_AUTO = 0
 XPRESS_COMBINE_SINGLE = 1
 XPRESS_COMBINE_ATOMIC = 2
 XPRESS_COMBINE_TWO_PASS = 3
+XPRESS_COMBINE_BALANCED = 4
 
 COMBINE_NAMES = {XPRESS_COMBINE_SINGLE: "single", XPRESS_COMBINE_ATOMIC: "atomic",
-                 XPRESS_COMBINE_TWO_PASS: "two_pass"}
+                 XPRESS_COMBINE_TWO_PASS: "two_pass", XPRESS_COMBINE_BALANCED: "balanced"}
 
 _lock = threading.Lock()
 _lib = None
