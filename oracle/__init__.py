@@ -67,6 +67,9 @@ def _load():
         lib.oracle_add_argmax_rows.argtypes = [
             _U16P, _U16P, _I64P] + [ctypes.c_int64] * 5
         lib.oracle_add_argmax_rows.restype = ctypes.c_int
+        lib.oracle_topc_argmax_to_blk.argtypes = [
+            _U16P, _U16P, _I64P, _I64P] + [ctypes.c_int64] * 3
+        lib.oracle_topc_argmax_to_blk.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -188,3 +191,23 @@ def add_argmax_rows_threaded(base, bias, rows: int, V: int, stride_base_r: int,
     for t in ts:
         t.join()
     return out
+
+
+def topc_argmax_to_blk(base_c, bias_c, cand, blk: np.ndarray, N: int, B: int, C: int) -> None:
+    """In-place top-C oracle on host arrays: for draft row r = n*(B-1) + j,
+    blk[n, 1+j] = cand[r, first argmax_c bf16(base_c[r, c] + bias_c[r, c])].
+    base_c / bias_c: uint16 bf16 patterns, cand: int64, all [N*(B-1), C]
+    contiguous; blk: C-contiguous int64 of N*B elements."""
+    base_c = _u16(base_c).reshape(-1)
+    bias_c = _u16(bias_c).reshape(-1)
+    cand = np.ascontiguousarray(cand, dtype=np.int64).reshape(-1)
+    rows = N * (B - 1)
+    if C < 1 or base_c.size < rows * C or bias_c.size < rows * C or cand.size < rows * C:
+        raise ValueError("top-C buffers do not hold N*(B-1)*C candidates")
+    if blk.dtype != np.int64 or not blk.flags.c_contiguous or blk.size != N * B:
+        raise ValueError("blk must be a C-contiguous int64 array of N*B elements")
+    rc = _load().oracle_topc_argmax_to_blk(
+        _p16(base_c), _p16(bias_c), cand.ctypes.data_as(_I64P), blk.ctypes.data_as(_I64P),
+        N, B, C)
+    if rc != 0:
+        raise ValueError("oracle rejected the sizes")

@@ -208,3 +208,32 @@ int oracle_add_argmax_rows(const uint16_t* base, const uint16_t* bias,
     }
     return 0;
 }
+
+/* ---------------------------------------------------------------------------
+ * Top-C readout (XPress kernels page, "_xpress_topc_argmax_to_blk_kernel" and
+ * "fused_topc_argmax_to_blk"): each draft row r = n*(B-1) + j carries C
+ * candidates -- their base logits base_c[r, c], refiner bias bias_c[r, c]
+ * and vocabulary ids cand[r, c], all three [N, B-1, C] contiguous.  The
+ * winner is the first c maximising bf16(base_c + bias_c) (the same element
+ * rule and tie rule as the full-vocabulary readout), and its id is written
+ * to blk[n, 1 + j]:
+ *     blk[n*B + 1 + j] = cand[r*C + first_argmax_c]
+ * Slot 0 and all other memory are untouched.  Returns 0, or -1 on sizes that
+ * describe no valid layout.
+ * ------------------------------------------------------------------------- */
+int oracle_topc_argmax_to_blk(const uint16_t* base_c, const uint16_t* bias_c,
+                              const int64_t* cand, int64_t* blk, int64_t N,
+                              int64_t B, int64_t C)
+{
+    if (N < 0 || B < 1 || C < 1) {
+        return -1;
+    }
+    int64_t rows = N * (B - 1);
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t n = r / (B - 1);
+        int64_t j = r % (B - 1);
+        int64_t best = oracle_add_argmax_row(base_c + r * C, bias_c + r * C, C);
+        blk[n * B + 1 + j] = cand[r * C + best];
+    }
+    return 0;
+}

@@ -321,3 +321,64 @@ def test_matches_torch_bf16_add_argmax(name, rows):
         oracle.add_argmax_to_blk(base, bias, blk, w.N, w.B, w.V, w.stride_base,
                                  w.stride_bias)
         assert np.array_equal(blk[:, 1:].reshape(-1), ref)
+
+
+def load_topc_rows():
+    out = []
+    with open(os.path.join(GOLDEN, "topc_rows.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, base, bias, cand, tok, why = [p.strip() for p in line.split(";", 5)]
+            base = np.array([int(x, 16) for x in base.split()], dtype=np.uint16)
+            bias = np.array([int(x, 16) for x in bias.split()], dtype=np.uint16)
+            cand = np.array([int(x) for x in cand.split()], dtype=np.int64)
+            out.append((name, base, bias, cand, int(tok), why))
+    return out
+
+
+TOPC_ROWS = load_topc_rows()
+
+
+@pytest.mark.parametrize("name,base,bias,cand,tok,why", TOPC_ROWS,
+                         ids=[c[0] for c in TOPC_ROWS])
+def test_topc_golden(name, base, bias, cand, tok, why):
+    C = base.size
+    blk = np.array([[-3, -1]], dtype=np.int64)
+    oracle.topc_argmax_to_blk(base, bias, cand, blk, 1, 2, C)
+    assert blk[0, 1] == tok, why
+    assert blk[0, 0] == -3
+    assert cand[exact_bf16.first_argmax(base, bias)] == tok, why
+
+
+@pytest.mark.parametrize("N,B,C", [(3, 5, 1), (2, 4, 7), (4, 16, 64), (2, 2, 4096)])
+def test_topc_planted_closed_form(N, B, C):
+    """Row r's unique maximum sits at c = r mod C, so blk[n, 1+j] must be
+    cand[r, r mod C] for r = n*(B-1) + j."""
+    g = np.random.Generator(np.random.PCG64(C))
+    rows = N * (B - 1)
+    base = (g.integers(-64, 64, size=(rows, C)) / 16.0).astype(np.float32)
+    base[np.arange(rows), np.arange(rows) % C] = 64.0
+    bias = (g.integers(-64, 64, size=(rows, C)) / 16.0).astype(np.float32)
+    cand = g.integers(0, 2 ** 40, size=(rows, C), dtype=np.int64)
+    blk = np.full((N, B), -1, dtype=np.int64)
+    blk[:, 0] = 77
+    oracle.topc_argmax_to_blk(workloads.f32_to_bf16_bits(base), workloads.f32_to_bf16_bits(bias),
+                              cand, blk, N, B, C)
+    want = cand[np.arange(rows), np.arange(rows) % C].reshape(N, B - 1)
+    assert np.array_equal(blk[:, 1:], want) and (blk[:, 0] == 77).all()
+
+
+@pytest.mark.parametrize("name", list(workloads.TOPC_WORKLOADS))
+def test_topc_matches_torch_add_argmax_gather(name):
+    """torch CPU: bf16 + bf16, argmax (first occurrence), gather of the id --
+    the top-C kernel's unfused spelling -- equals the oracle on every row."""
+    w = workloads.TOPC_WORKLOADS[name]
+    base_c, bias_c, cand, blk = workloads.generate_topc(w)
+    a = torch.from_numpy(base_c.view(np.int16)).view(torch.bfloat16)
+    b = torch.from_numpy(bias_c.view(np.int16)).view(torch.bfloat16)
+    pos = torch.argmax(a + b, dim=-1)
+    ref = torch.gather(torch.from_numpy(cand), 1, pos[:, None])[:, 0].numpy()
+    oracle.topc_argmax_to_blk(base_c, bias_c, cand, blk, w.N, w.B, w.C)
+    assert np.array_equal(blk[:, 1:].reshape(-1), ref)

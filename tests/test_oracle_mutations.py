@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import exact_bf16
-from test_oracle import ARGMAX_ROWS, ROUNDING
+from test_oracle import ARGMAX_ROWS, ROUNDING, TOPC_ROWS
 from vocab_wide_add_amd import workloads
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -39,6 +39,10 @@ MUTATIONS = {
                        "oracle_add_argmax_row(base + r * V,\n"
                        "                                                   bias + r * V, V);"),
     "sign_dropped": ("return sign ? -mag : mag;", "return mag;"),
+    "topc_position_not_id": ("blk[n * B + 1 + j] = cand[r * C + best];",
+                             "blk[n * B + 1 + j] = best;"),
+    "topc_wrong_row": ("blk[n * B + 1 + j] = cand[r * C + best];",
+                       "blk[n * B + 1 + j] = cand[best];"),
 }
 
 
@@ -58,6 +62,8 @@ def _build_mutant(tmp_path, name):
     lib.oracle_add_argmax_row.restype = ctypes.c_int64
     lib.oracle_add_argmax_to_blk.argtypes = [U16P, U16P, I64P] + [ctypes.c_int64] * 5
     lib.oracle_add_argmax_to_blk.restype = ctypes.c_int
+    lib.oracle_topc_argmax_to_blk.argtypes = [U16P, U16P, I64P, I64P] + [ctypes.c_int64] * 3
+    lib.oracle_topc_argmax_to_blk.restype = ctypes.c_int
     return lib
 
 
@@ -89,6 +95,23 @@ def _pins_pass(lib) -> bool:
         want = (np.arange(N * (B - 1)) % V).reshape(N, B - 1)
         if not np.array_equal(blk[:, 1:], want) or not np.array_equal(blk[:, 0], anchors):
             return False
+    for _, base, bias, cand, tok, _ in TOPC_ROWS:
+        blk = np.array([[-3, -1]], dtype=np.int64)
+        base, bias, cand = (np.ascontiguousarray(x) for x in (base, bias, cand))
+        lib.oracle_topc_argmax_to_blk(base.ctypes.data_as(U16P), bias.ctypes.data_as(U16P),
+                                      cand.ctypes.data_as(I64P), blk.ctypes.data_as(I64P),
+                                      1, 2, base.size)
+        if blk[0, 1] != tok or blk[0, 0] != -3:
+            return False
+    # two rows of two candidates: row 1's winner must come from row 1's ids
+    base = np.array([0x3F80, 0x4000, 0x4000, 0x3F80], dtype=np.uint16)
+    bias = np.zeros(4, dtype=np.uint16)
+    cand = np.array([10, 11, 20, 21], dtype=np.int64)
+    blk = np.full((1, 3), -1, dtype=np.int64)
+    lib.oracle_topc_argmax_to_blk(base.ctypes.data_as(U16P), bias.ctypes.data_as(U16P),
+                                  cand.ctypes.data_as(I64P), blk.ctypes.data_as(I64P), 1, 3, 2)
+    if list(blk[0]) != [-1, 11, 20]:
+        return False
     return True
 
 
@@ -107,6 +130,8 @@ def test_unmutated_oracle_passes_the_pins(tmp_path):
     lib.oracle_add_argmax_row.restype = ctypes.c_int64
     lib.oracle_add_argmax_to_blk.argtypes = [U16P, U16P, I64P] + [ctypes.c_int64] * 5
     lib.oracle_add_argmax_to_blk.restype = ctypes.c_int
+    lib.oracle_topc_argmax_to_blk.argtypes = [U16P, U16P, I64P, I64P] + [ctypes.c_int64] * 3
+    lib.oracle_topc_argmax_to_blk.restype = ctypes.c_int
     assert _pins_pass(lib)
 
 

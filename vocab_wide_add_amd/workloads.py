@@ -170,3 +170,78 @@ def planted(N: int, B: int, V: int, seed: int = 0, pad: int = 0):
     blk = np.full((N, B), -1, dtype=np.int64)
     blk[:, 0] = g.integers(0, V, size=N)
     return base_bits, bias_bits, blk
+
+
+# ---------------------------------------------------------------------------
+# Top-C readout inputs: per draft row, C candidates with their base logits,
+# refiner bias and vocabulary ids, all [N*(B-1), C] contiguous.
+# ---------------------------------------------------------------------------
+
+
+@dataclasses.dataclass(frozen=True)
+class TopCWorkload:
+    name: str
+    N: int
+    B: int
+    C: int
+    seed: int
+    vocab: int = 152064
+    ties: bool = False  # integer-valued logits: many exact ties
+
+    @property
+    def rows(self) -> int:
+        return self.N * (self.B - 1)
+
+    @property
+    def bytes_read(self) -> int:
+        """Algorithmic bytes of one readout: two bf16 values per candidate
+        plus the winner's 8-byte id per row."""
+        return self.rows * (self.C * 4 + 8)
+
+
+TOPC_WORKLOADS = {
+    w.name: w
+    for w in [
+        TopCWorkload("topc_n32_b16_c64", 32, 16, 64, 10),
+        TopCWorkload("topc_n32_b16_c256", 32, 16, 256, 11),
+        TopCWorkload("topc_n32_b16_c1024", 32, 16, 1024, 12),
+        TopCWorkload("topc_n32_b16_c4096", 32, 16, 4096, 13),
+        TopCWorkload("topc_ties_n32_b16_c256", 32, 16, 256, 14, ties=True),
+    ]
+}
+
+
+def generate_topc(w: TopCWorkload):
+    """Top-C inputs shaped like a real candidate list.
+
+    Recipe (``SeedSequence(seed).spawn(2)``: a logits stream and an id
+    stream): for every row, a full vocabulary of base logits is drawn,
+    N(0, 4^2) in float32 (or integers uniform on [-3, 3] for the tie
+    workload); the C largest become the candidates -- their ids, in
+    descending order of base logit, form cand, and their values base_c.  The
+    refiner bias on the candidates is N(0, 1^2) (integers on [-3, 3] for the
+    tie workload).  Anchors are uniform on [0, vocab).  Returns
+    ``(base_c, bias_c, cand, blk)`` with blk's draft slots at -1.
+    """
+    s_val, s_ids = np.random.SeedSequence(w.seed).spawn(2)
+    g = np.random.Generator(np.random.PCG64(s_val))
+    gi = np.random.Generator(np.random.PCG64(s_ids))
+    rows, C, V = w.rows, w.C, w.vocab
+    base_c = np.empty((rows, C), dtype=np.float32)
+    cand = np.empty((rows, C), dtype=np.int64)
+    for r in range(rows):
+        if w.ties:
+            full = g.integers(-3, 4, size=V).astype(np.float32)
+        else:
+            full = g.standard_normal(V, dtype=np.float32) * np.float32(4.0)
+        top = np.argpartition(-full, C - 1)[:C]
+        top = top[np.argsort(-full[top], kind="stable")]
+        cand[r] = top
+        base_c[r] = full[top]
+    if w.ties:
+        bias_c = g.integers(-3, 4, size=(rows, C)).astype(np.float32)
+    else:
+        bias_c = g.standard_normal((rows, C), dtype=np.float32)
+    blk = np.full((w.N, w.B), -1, dtype=np.int64)
+    blk[:, 0] = gi.integers(0, V, size=w.N)
+    return f32_to_bf16_bits(base_c), f32_to_bf16_bits(bias_c), cand, blk
