@@ -33,7 +33,8 @@ MUTATIONS = {
     "overflow_saturates": ("return sign | 0x7F80; /* overflow to infinity */",
                            "return sign | 0x7F7F; /* overflow to infinity */"),
     "anchor_overwritten": ("blk[n * B + 1 + b] =", "blk[n * B + b] ="),
-    "row_to_block_by_B": ("int64_t n = r / (B - 1);", "int64_t n = r / B;"),
+    "row_to_block_by_B": ("int64_t n = r / (B - 1);\n        int64_t b = r % (B - 1);",
+                          "int64_t n = r / B;\n        int64_t b = r % (B - 1);"),
     "stride_ignored": ("oracle_add_argmax_row(base + r * stride_base_r,\n"
                        "                                                   bias + r * stride_bias_r, V);",
                        "oracle_add_argmax_row(base + r * V,\n"
