@@ -20,7 +20,12 @@ The default warmup (300 steps, ~14 ms) covers the clock ramp measured on
 MI355X: under sustained back-to-back calls the readout settles after about
 200 calls.
 
+``--op topc --topc-c C`` times the top-C readout (``xpress_topc_argmax_to_blk``)
+on the synthetic top-C workload with C candidates per row instead; the
+default is the full-vocabulary readout.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--op readout|topc] [--topc-c C]
 """
 from __future__ import annotations
 
@@ -105,12 +110,177 @@ def copy_probe(nbytes: int, reps: int):
     print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}))
 
 
+def time_steps(step, steps: int, warmup: int, stream):
+    """Warm up, then time ``steps`` calls twice: region 1 back to back (wall
+    clock and one HIP event pair on the launch stream around the region),
+    region 2 with a HIP event pair around every call.  Returns (wall seconds
+    of region 1, GPU seconds of region 1, sorted per-call GPU seconds of
+    region 2)."""
+    import torch
+    for k in range(warmup):
+        step(k)
+    torch.cuda.synchronize()
+    log("timing %d steps" % steps)
+    r0 = torch.cuda.Event(enable_timing=True)
+    r1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    r0.record(stream)
+    for k in range(steps):
+        step(k)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    region_gpu = r0.elapsed_time(r1) * 1e-3
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for k in range(steps):
+        starts[k].record(stream)
+        step(k)
+        ends[k].record(stream)
+    torch.cuda.synchronize()
+    durs = sorted(a.elapsed_time(b) * 1e-3 for a, b in zip(starts, ends))
+    return wall, region_gpu, durs
+
+
+def result_line(metric, name, config, bytes_per_call, rows, steps, warmup, wall, region_gpu,
+                durs, launches, traffic):
+    kavg = sum(durs) / len(durs)
+    # the kernel's average duration: GPU time of timed region 1 (HIP events
+    # on the launch stream) per launch.  The default workload's plan is one
+    # launch per step; the per-launch event pairs of region 2 carry ~2 us of
+    # event overhead each and are reported beside it.
+    kernel_avg = region_gpu / steps / max(1, launches)
+    achieved = bytes_per_call / max(1, launches) / kernel_avg / 1e9
+    value = bytes_per_call * steps / wall / 1e9
+    return {
+        "metric": metric,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(wall / steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": config,
+        "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "rows_per_s": round(rows * steps / wall, 1),
+        "region_gpu_us_per_step": round(region_gpu / steps * 1e6, 3),
+        "kernel_us_region_avg": round(kernel_avg * 1e6, 3),
+        "kernel_us_event_pairs": {"avg": round(kavg * 1e6, 3), "min": round(durs[0] * 1e6, 3),
+                                  "p50": round(durs[len(durs) // 2] * 1e6, 3),
+                                  "p90": round(durs[int(len(durs) * 0.9)] * 1e6, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": None,
+    }
+
+
+def bench_readout(args, np, torch, native, workloads):
+    name = args.workload or workloads.BENCH_WORKLOAD
+    w = workloads.WORKLOADS[name]
+    log("generating %s" % name)
+    base, bias, blk0 = workloads.generate(w)
+    footprint = base.nbytes + bias.nbytes
+    sets = max(1, math.ceil(2 * LLC_BYTES / footprint) + 1)
+    log("uploading %d input sets of %.1f MB" % (sets, footprint / 1e6))
+    b_cpu = torch.from_numpy(base.view(np.int16))
+    i_cpu = torch.from_numpy(bias.view(np.int16))
+    dev = [(b_cpu.cuda(), i_cpu.cuda(), torch.from_numpy(blk0).cuda()) for _ in range(sets)]
+    stream = torch.cuda.current_stream()
+    plan = native.xpress_describe_plan(dev[0][0], dev[0][1], w.N, w.B, w.V,
+                                       w.stride_base, w.stride_bias)
+    native.xpress_reserve(w.N, w.B, w.V, stream=stream)
+
+    def step(k):
+        b, i, blk = dev[k % sets]
+        native.xpress_add_argmax_to_blk(b, i, blk, w.N, w.B, w.V, w.stride_base,
+                                        w.stride_bias, stream=stream)
+
+    wall, region_gpu, durs = time_steps(step, args.steps, args.warmup, stream)
+    got = dev[(args.steps - 1) % sets][2].cpu().numpy()
+    config = {"workload": name, "N": w.N, "B": w.B, "V": w.V, "rows": w.rows,
+              "stride_base": w.stride_base, "stride_bias": w.stride_bias,
+              "bytes_per_step": w.bytes_read, "input_sets": sets, "plan": plan}
+    out = result_line("effective HBM GB/s (+ %% of peak) and rows/s, add+argmax N=%d B=%d V=%d"
+                      % (w.N, w.B, w.V), name, config, w.bytes_read, w.rows, args.steps,
+                      args.warmup, wall, region_gpu, durs, plan["launches"], traffic_for(name))
+    if not args.no_cpu_baseline:
+        log("cpu baseline")
+        cb, nrows, ans = cpu_baseline(base, bias, w, args.cpu_seconds)
+        out["cpu_baseline"] = cb
+        out["checked_rows"] = nrows
+        out["checked_equal"] = bool(np.array_equal(got[:, 1:].reshape(-1)[:nrows], ans))
+        if not out["checked_equal"]:
+            log("MISMATCH against the oracle on the sampled rows")
+    return out
+
+
+def bench_topc(args, np, torch, native, workloads):
+    name = "topc_n32_b16_c%d" % args.topc_c
+    w = workloads.TOPC_WORKLOADS[name]
+    log("generating %s" % name)
+    base_c, bias_c, cand, blk0 = workloads.generate_topc(w)
+    footprint = base_c.nbytes + bias_c.nbytes + cand.nbytes
+    # the inputs are small; rotate over enough copies to leave the 256 MB
+    # last-level cache, capped at 64 copies
+    sets = int(min(64, max(1, math.ceil(2 * LLC_BYTES / footprint) + 1)))
+    log("uploading %d input sets of %.2f MB" % (sets, footprint / 1e6))
+    b_cpu = torch.from_numpy(base_c.view(np.int16))
+    i_cpu = torch.from_numpy(bias_c.view(np.int16))
+    c_cpu = torch.from_numpy(cand)
+    dev = [(b_cpu.cuda(), i_cpu.cuda(), c_cpu.cuda(), torch.from_numpy(blk0).cuda())
+           for _ in range(sets)]
+    stream = torch.cuda.current_stream()
+    plan = native.xpress_describe_plan(dev[0][0], dev[0][1], w.N, w.B, w.C, w.C, w.C)
+    native.xpress_reserve(w.N, w.B, w.C, stream=stream)
+
+    def step(k):
+        b, i, c, blk = dev[k % sets]
+        native.xpress_topc_argmax_to_blk(b, i, c, blk, w.N, w.B, w.C, stream=stream)
+
+    wall, region_gpu, durs = time_steps(step, args.steps, args.warmup, stream)
+    config = {"workload": name, "op": "topc", "N": w.N, "B": w.B, "C": w.C, "rows": w.rows,
+              "bytes_per_step": w.bytes_read, "input_sets": sets, "plan": plan}
+    out = result_line("top-C readout: effective GB/s and rows/s, N=%d B=%d C=%d"
+                      % (w.N, w.B, w.C), name, config, w.bytes_read, w.rows, args.steps,
+                      args.warmup, wall, region_gpu, durs, plan["launches"], None)
+    got = dev[(args.steps - 1) % sets][3].cpu().numpy()
+    if not args.no_cpu_baseline:
+        import oracle
+        log("cpu baseline")
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            want = blk0.copy()
+            oracle.topc_argmax_to_blk(base_c, bias_c, cand, want, w.N, w.B, w.C)
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= min(args.cpu_seconds, 5.0) or passes >= 1000:
+                break
+        out["cpu_baseline"] = {"value": round(passes * w.bytes_read / dt / 1e9, 3),
+                               "unit": "GB/s", "cores": 1, "kind": "oracle",
+                               "rows_per_s": round(passes * w.rows / dt, 1),
+                               "sample": "all %d rows of %s, %d passes, %.1f s, one thread"
+                                         % (w.rows, name, passes, dt)}
+        out["checked_rows"] = w.rows
+        out["checked_equal"] = bool(np.array_equal(got, want))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--op", choices=["readout", "topc"], default="readout")
+    ap.add_argument("--topc-c", type=int, default=1024, choices=[64, 256, 1024, 4096])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU work budget of the oracle baseline leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -134,113 +304,10 @@ def main():
     if args.copy_probe_bytes:
         copy_probe(args.copy_probe_bytes, max(1, args.steps))
         return
-
-    name = args.workload or workloads.BENCH_WORKLOAD
-    w = workloads.WORKLOADS[name]
-    log("generating %s" % name)
-    base, bias, blk0 = workloads.generate(w)
-    bytes_per_call = w.bytes_read
-    footprint = base.nbytes + bias.nbytes
-    sets = max(1, math.ceil(2 * LLC_BYTES / footprint) + 1)
-    log("uploading %d input sets of %.1f MB" % (sets, footprint / 1e6))
-    dev = []
-    b_cpu = torch.from_numpy(base.view(np.int16))
-    i_cpu = torch.from_numpy(bias.view(np.int16))
-    for _ in range(sets):
-        dev.append((b_cpu.cuda(), i_cpu.cuda(), torch.from_numpy(blk0).cuda()))
-    stream = torch.cuda.current_stream()
-    plan = native.xpress_describe_plan(dev[0][0], dev[0][1], w.N, w.B, w.V,
-                                       w.stride_base, w.stride_bias)
-    native.xpress_reserve(w.N, w.B, w.V, stream=stream)
-
-    def step(k):
-        b, i, blk = dev[k % sets]
-        native.xpress_add_argmax_to_blk(b, i, blk, w.N, w.B, w.V, w.stride_base,
-                                        w.stride_bias, stream=stream)
-
-    for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
-
-    # timed region 1 (throughput): K back-to-back steps, wall clock and a
-    # HIP event pair on the launch stream around the whole region
-    log("timing %d steps" % args.steps)
-    r0 = torch.cuda.Event(enable_timing=True)
-    r1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    r0.record(stream)
-    for k in range(args.steps):
-        step(k)
-    r1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    region_gpu = r0.elapsed_time(r1) * 1e-3
-
-    # timed region 2 (per launch): the same K steps, each bracketed by its
-    # own HIP event pair on the launch stream, for the kernel's duration
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for k in range(args.steps):
-        starts[k].record(stream)
-        step(k)
-        ends[k].record(stream)
-    torch.cuda.synchronize()
-    durs = sorted(s.elapsed_time(e) * 1e-3 for s, e in zip(starts, ends))
-    kavg = sum(durs) / len(durs)
-
-    # answers of the last set touched, for the check against the oracle
-    got = dev[(args.steps - 1) % sets][2].cpu().numpy()
-
-    ms_per_step = wall / args.steps * 1e3
-    value = bytes_per_call * args.steps / wall / 1e9
-    # the readout kernel's average duration: GPU time of timed region 1 (HIP
-    # events on the launch stream) per launch.  Every plan of the default
-    # workload is one launch per step; the per-launch event pairs of region 2
-    # carry ~2 us of event overhead each and are reported beside it.
-    kernel_avg = region_gpu / args.steps / max(1, plan["launches"])
-    achieved = bytes_per_call / max(1, plan["launches"]) / kernel_avg / 1e9
-    traffic = traffic_for(name)
-    out = {
-        "metric": "effective HBM GB/s (+ %% of peak) and rows/s, add+argmax N=%d B=%d V=%d"
-                  % (w.N, w.B, w.V),
-        "value": round(value, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": name, "N": w.N, "B": w.B, "V": w.V, "rows": w.rows,
-                   "stride_base": w.stride_base, "stride_bias": w.stride_bias,
-                   "bytes_per_step": bytes_per_call, "input_sets": sets,
-                   "plan": plan},
-        "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "rows_per_s": round(w.rows * args.steps / wall, 1),
-        "region_gpu_us_per_step": round(region_gpu / args.steps * 1e6, 3),
-        "kernel_us_region_avg": round(kernel_avg * 1e6, 3),
-        "kernel_us_event_pairs": {"avg": round(kavg * 1e6, 3), "min": round(durs[0] * 1e6, 3),
-                      "p50": round(durs[len(durs) // 2] * 1e6, 3),
-                      "p90": round(durs[int(len(durs) * 0.9)] * 1e6, 3)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
-        "cpu_baseline": None,
-    }
-    if not args.no_cpu_baseline:
-        log("cpu baseline")
-        cb, nrows, ans = cpu_baseline(base, bias, w, args.cpu_seconds)
-        out["cpu_baseline"] = cb
-        flat = got[:, 1:].reshape(-1)[:nrows]
-        out["checked_rows"] = nrows
-        out["checked_equal"] = bool(np.array_equal(flat, ans))
-        if not out["checked_equal"]:
-            log("MISMATCH against the oracle on the sampled rows")
+    if args.op == "topc":
+        out = bench_topc(args, np, torch, native, workloads)
+    else:
+        out = bench_readout(args, np, torch, native, workloads)
     print(json.dumps(out))
     sys.stdout.flush()
 

@@ -86,6 +86,31 @@ int xpress_add_argmax_to_blk(const uint16_t* base, const uint16_t* bias,
                              hipStream_t stream);
 
 /*
+ * xpress_topc_argmax_to_blk -- the top-C readout (XPress kernels page,
+ * "_xpress_topc_argmax_to_blk_kernel" and "fused_topc_argmax_to_blk"): each
+ * draft row r = n*(B-1) + j carries C candidates; the first candidate
+ * maximising bf16(base_c[r, c] + bias_c[r, c]) -- same element and tie rule
+ * as above -- wins, and its vocabulary id is written:
+ *
+ *     blk[n, 1 + j] = cand[r, first argmax_c bf16(base_c[r, c] + bias_c[r, c])]
+ *
+ *   base_c, bias_c  device pointers to bf16 bit patterns, [N, B-1, C]
+ *                   contiguous (row r at r*C).  Read only.
+ *   cand            device pointer to int64 ids, [N, B-1, C] contiguous.
+ *                   Read only; the winner's id is copied as is.
+ *   blk             device pointer to int64 [N, B]; slots 1..B-1 written,
+ *                   slot 0 untouched.  Must not overlap any input.
+ *   N, B            as above; C >= 1 candidates per row (<= 2^31 - 1).
+ *   stream          HIP stream (0 = the null stream).
+ *
+ * Asynchronous; same plans, workspace, no-op and error rules as
+ * xpress_add_argmax_to_blk (with V = C and row strides C).
+ */
+int xpress_topc_argmax_to_blk(const uint16_t* base_c, const uint16_t* bias_c,
+                              const int64_t* cand, int64_t* blk, int64_t N,
+                              int64_t B, int64_t C, hipStream_t stream);
+
+/*
  * xpress_reserve -- pre-allocate the workspace the readout would use for
  * (N, B, V) on `stream`'s device and stream, so that a later call -- e.g.
  * one being captured into a HIP graph -- allocates nothing.  Synchronous.

@@ -8,7 +8,14 @@ import re
 
 import pytest
 
+from conftest import gpu_available
 from vocab_wide_add_amd import native
+
+# The argument-validation tests below pass made-up addresses that must be
+# rejected before any launch.  They only run where there is no GPU, so a
+# mistake in a test tuple can never put a kernel on a device with bad
+# pointers; the GPU suite checks the same errors with real buffers.
+no_gpu_only = pytest.mark.skipif(gpu_available(), reason="fake-pointer checks run without a GPU")
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "xpress_argmax.h")
@@ -90,12 +97,14 @@ def test_plan_override_round_trip():
     (4096, 256, 268, 1, 2, 8, 8, 8),       # blk overlaps bias
     (256, 256, 512, 1, 2, 2 ** 31, 2 ** 31, 2 ** 31),  # V too large
 ])
+@no_gpu_only
 def test_invalid_arguments_rejected_before_launch(args):
     # validation happens before any HIP call, so this runs without a GPU
     lib = native.load()
     assert lib.xpress_add_argmax_to_blk(*args, None) == native.XPRESS_EINVAL
 
 
+@no_gpu_only
 def test_no_rows_is_ok_without_pointers():
     lib = native.load()
     assert lib.xpress_add_argmax_to_blk(0, 0, 0, 0, 16, 152064, 152064, 152064, None) == 0
@@ -107,3 +116,23 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(native, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(ImportError):
         native.load()
+
+
+@pytest.mark.parametrize("args", [
+    (256, 256, 0, 4096, 1, 2, 8),          # null cand with rows
+    (256, 256, 1024, 1040, 1, 2, 8),       # blk [1040, 1056) overlaps cand [1024, 1088)
+    (256, 256, 1024, 4096, 1, 2, 0),       # C < 1
+    (256, 256, 1024, 4096, -1, 2, 8),      # N < 0
+    (0, 256, 1024, 4096, 1, 2, 8),         # null base_c
+])
+@no_gpu_only
+def test_topc_invalid_arguments_rejected_before_launch(args):
+    lib = native.load()
+    assert lib.xpress_topc_argmax_to_blk(*args, None) == native.XPRESS_EINVAL
+
+
+@no_gpu_only
+def test_topc_no_rows_is_ok_without_pointers():
+    lib = native.load()
+    assert lib.xpress_topc_argmax_to_blk(0, 0, 0, 0, 0, 16, 256, None) == 0
+    assert lib.xpress_topc_argmax_to_blk(0, 0, 0, 0, 32, 1, 256, None) == 0

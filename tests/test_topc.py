@@ -1,0 +1,124 @@
+"""Parity of the HIP top-C readout with the CPU oracle, through the C-ABI.
+
+blk[n, 1+j] must equal cand[r, first argmax_c bf16(base_c + bias_c)] bit for
+bit, with slot 0 and everything outside blk's draft slots untouched.
+"""
+import numpy as np
+import pytest
+
+from conftest import gpu_available
+from gpu_util import Plan, say, to_dev
+import oracle
+from vocab_wide_add_amd import native, workloads
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+COMBINES = [native.XPRESS_COMBINE_SINGLE, native.XPRESS_COMBINE_ATOMIC,
+            native.XPRESS_COMBINE_TWO_PASS, native.XPRESS_COMBINE_BALANCED]
+
+
+def oracle_topc(base_c, bias_c, cand, blk0, N, B, C):
+    want = blk0.copy()
+    oracle.topc_argmax_to_blk(base_c, bias_c, cand, want, N, B, C)
+    return want
+
+
+def gpu_topc(base_d, bias_d, cand_d, blk0, N, B, C):
+    import torch
+    blk_d = to_dev(blk0)
+    native.xpress_topc_argmax_to_blk(base_d, bias_d, cand_d, blk_d, N, B, C)
+    torch.cuda.synchronize()
+    return blk_d.cpu().numpy()
+
+
+_cache = {}
+
+
+def case(name):
+    if name not in _cache:
+        w = workloads.TOPC_WORKLOADS[name]
+        base_c, bias_c, cand, blk0 = workloads.generate_topc(w)
+        want = oracle_topc(base_c, bias_c, cand, blk0, w.N, w.B, w.C)
+        _cache[name] = (w, blk0, to_dev(base_c), to_dev(bias_c), to_dev(cand), want)
+    return _cache[name]
+
+
+@pytest.mark.parametrize("name", list(workloads.TOPC_WORKLOADS))
+def test_topc_workload_default_plan(name):
+    w, blk0, bd, id_, cd, want = case(name)
+    say("topc %s default plan" % name)
+    got = gpu_topc(bd, id_, cd, blk0, w.N, w.B, w.C)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("name", ["topc_n32_b16_c256", "topc_ties_n32_b16_c256",
+                                  "topc_n32_b16_c4096"])
+@pytest.mark.parametrize("combine", COMBINES)
+@pytest.mark.parametrize("threads,splits", [(64, 0), (256, 0), (1024, 0), (64, 3), (128, 2)])
+def test_topc_every_plan(name, combine, threads, splits):
+    w, blk0, bd, id_, cd, want = case(name)
+    say("topc %s combine=%d threads=%d splits=%d" % (name, combine, threads, splits))
+    with Plan(combine, splits, threads):
+        got = gpu_topc(bd, id_, cd, blk0, w.N, w.B, w.C)
+    assert np.array_equal(got, want)
+
+
+def _rows(rows, C, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    a = g.integers(-3, 4, size=(rows, C)).astype(np.float32)
+    b = g.integers(-3, 4, size=(rows, C)).astype(np.float32)
+    cand = g.integers(0, 2 ** 40, size=(rows, C), dtype=np.int64)
+    return workloads.f32_to_bf16_bits(a), workloads.f32_to_bf16_bits(b), cand
+
+
+@pytest.mark.parametrize("C", [1, 2, 7, 8, 9, 63, 64, 65, 100, 1000, 4097])
+@pytest.mark.parametrize("combine", COMBINES)
+def test_topc_ragged_candidates(C, combine):
+    N, B = 5, 9
+    base_c, bias_c, cand = _rows(N * (B - 1), C, C)
+    blk0 = np.full((N, B), -1, dtype=np.int64)
+    blk0[:, 0] = 123
+    want = oracle_topc(base_c, bias_c, cand, blk0, N, B, C)
+    bd, id_, cd = to_dev(base_c), to_dev(bias_c), to_dev(cand)
+    say("topc ragged C=%d combine=%d" % (C, combine))
+    for splits in (0, 2):
+        with Plan(combine, splits, 64):
+            got = gpu_topc(bd, id_, cd, blk0, N, B, C)
+        assert np.array_equal(got, want), (C, combine, splits)
+
+
+def test_topc_planted_and_guard_cells():
+    import torch
+    N, B, C = 32, 16, 512
+    rows = N * (B - 1)
+    g = np.random.Generator(np.random.PCG64(5))
+    base = (g.integers(-64, 64, size=(rows, C)) / 16.0).astype(np.float32)
+    base[np.arange(rows), np.arange(rows) % C] = 64.0
+    bias = (g.integers(-64, 64, size=(rows, C)) / 16.0).astype(np.float32)
+    cand = g.integers(0, 152064, size=(rows, C), dtype=np.int64)
+    guard = 0x3C3C3C3C3C3C3C3C
+    buf = np.full(N * B + 64, guard, dtype=np.int64)
+    buf[32:32 + N * B] = np.tile(np.array([9] + [-1] * (B - 1)), N)
+    buf_d = to_dev(buf)
+    say("topc planted + guard cells")
+    native.xpress_topc_argmax_to_blk(to_dev(workloads.f32_to_bf16_bits(base)),
+                                     to_dev(workloads.f32_to_bf16_bits(bias)), to_dev(cand),
+                                     buf_d.data_ptr() + 32 * 8, N, B, C)
+    torch.cuda.synchronize()
+    out = buf_d.cpu().numpy()
+    assert (out[:32] == guard).all() and (out[32 + N * B:] == guard).all()
+    blk = out[32:32 + N * B].reshape(N, B)
+    assert (blk[:, 0] == 9).all()
+    assert np.array_equal(blk[:, 1:].reshape(-1), cand[np.arange(rows), np.arange(rows) % C])
+
+
+def test_topc_invalid_arguments_raise():
+    import torch
+    x = torch.zeros(64, dtype=torch.int16, device="cuda")
+    c = torch.zeros(64, dtype=torch.int64, device="cuda")
+    blk = torch.zeros(4, dtype=torch.int64, device="cuda")
+    with pytest.raises(native.XpressError):
+        native.xpress_topc_argmax_to_blk(x, x, 0, blk, 1, 2, 8)
+    with pytest.raises(native.XpressError):
+        native.xpress_topc_argmax_to_blk(x, x, c, c, 1, 2, 8)  # blk aliases cand

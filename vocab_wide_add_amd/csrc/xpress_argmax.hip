@@ -285,16 +285,21 @@ struct RowArgs {
     uint32_t splits;      // workgroups per row
     uint64_t* keys;       // ATOMIC: [rows] key-and-count words;
                           // TWO_PASS: [rows, splits] key table
+    const int64_t* cand;  // top-C readout: [rows, V] candidate ids, else null
 };
 
 enum Combine { kSingle = XPRESS_COMBINE_SINGLE, kAtomic = XPRESS_COMBINE_ATOMIC,
                kTwoPass = XPRESS_COMBINE_TWO_PASS, kBalanced = XPRESS_COMBINE_BALANCED };
 
+// Row r = n*(B-1) + b writes slot 1 + b of block n.  The full-vocabulary
+// readout writes the winning position (a vocabulary id); the top-C readout
+// writes the winning candidate's id, cand[r, position].
 __device__ __forceinline__ void write_blk(const RowArgs& a, uint32_t row, int64_t idx)
 {
     const uint32_t n = row / a.bm1;
     const uint32_t b = row - n * a.bm1;
-    a.blk[(int64_t)n * (a.bm1 + 1) + 1 + b] = idx;
+    const int64_t tok = a.cand ? a.cand[(int64_t)row * a.V + idx] : idx;
+    a.blk[(int64_t)n * (a.bm1 + 1) + 1 + b] = tok;
 }
 
 // Fold one workgroup's candidate key into its row's 64-bit word, which holds
@@ -737,7 +742,8 @@ bool ranges_overlap(const void* p0, size_t n0, const void* p1, size_t n1)
 }
 
 int validate(const uint16_t* base, const uint16_t* bias, const int64_t* blk, int64_t N,
-             int64_t B, int64_t V, int64_t sb, int64_t sbi, int64_t* rows_out)
+             int64_t B, int64_t V, int64_t sb, int64_t sbi, const int64_t* cand,
+             int64_t* rows_out)
 {
     if (N < 0 || B < 1 || V < 1 || V > 0x7FFFFFFFll || sb < V || sbi < V) {
         return XPRESS_EINVAL;
@@ -748,7 +754,7 @@ int validate(const uint16_t* base, const uint16_t* bias, const int64_t* blk, int
     if (rows == 0) return XPRESS_OK;
     if (rows > 0x7FFFFFFFll || N > INT64_MAX / B) return XPRESS_EINVAL;
     if (!base || !bias || !blk) return XPRESS_EINVAL;
-    if ((rows - 1) > (INT64_MAX / 2 - V) / sb || (rows - 1) > (INT64_MAX / 2 - V) / sbi) {
+    if ((rows - 1) > (INT64_MAX / 8 - V) / sb || (rows - 1) > (INT64_MAX / 8 - V) / sbi) {
         return XPRESS_EINVAL;
     }
     const size_t base_bytes = (size_t)((rows - 1) * sb + V) * 2u;
@@ -757,6 +763,53 @@ int validate(const uint16_t* base, const uint16_t* bias, const int64_t* blk, int
     if (ranges_overlap(blk, blk_bytes, base, base_bytes) ||
         ranges_overlap(blk, blk_bytes, bias, bias_bytes)) {
         return XPRESS_EINVAL;
+    }
+    if (cand != nullptr) {
+        // candidate ids are [rows, V] contiguous, like the logits
+        const size_t cand_bytes = (size_t)(rows * V) * 8u;
+        if (ranges_overlap(blk, blk_bytes, cand, cand_bytes)) return XPRESS_EINVAL;
+    }
+    return XPRESS_OK;
+}
+
+// Plan, workspace and launches shared by both readouts.
+int run_readout(const uint16_t* base, const uint16_t* bias, const int64_t* cand, int64_t* blk,
+                int64_t N, int64_t B, int64_t V, int64_t sb, int64_t sbi, hipStream_t stream)
+{
+    int64_t rows = 0;
+    int rc = validate(base, bias, blk, N, B, V, sb, sbi, cand, &rows);
+    if (rc != XPRESS_OK || rows == 0) return rc;
+
+    const Plan p = make_plan(base, bias, rows, V, sb, sbi);
+    RowArgs a;
+    a.base = base;
+    a.bias = bias;
+    a.blk = blk;
+    a.stride_base = sb;
+    a.stride_bias = sbi;
+    a.rows = (uint32_t)rows;
+    a.bm1 = (uint32_t)(B - 1);
+    a.V = (uint32_t)V;
+    a.splits = (uint32_t)p.splits;
+    a.keys = nullptr;
+    a.cand = cand;
+
+    if (p.combine != kSingle) {
+        Workspace* w = nullptr;
+        const int64_t table = (p.combine == kTwoPass) ? rows * p.splits : 0;
+        const bool words = (p.combine == kAtomic || p.combine == kBalanced);
+        rc = ensure_workspace(stream, words ? rows : 0, table, &w);
+        if (rc != XPRESS_OK) return rc;
+        a.keys = words ? w->keys : w->table;
+    }
+
+    hipError_t e = launch_plan(a, p, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    if (p.combine == kTwoPass) {
+        const uint32_t grid = (uint32_t)((rows + 255) / 256 < 65536 ? (rows + 255) / 256 : 65536);
+        hipLaunchKernelGGL(reduce_keys_kernel, dim3(grid), dim3(256), 0, stream, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e);
     }
     return XPRESS_OK;
 }
@@ -769,45 +822,16 @@ int xpress_add_argmax_to_blk(const uint16_t* base, const uint16_t* bias, int64_t
                              int64_t N, int64_t B, int64_t V, int64_t stride_base_r,
                              int64_t stride_bias_r, hipStream_t stream)
 {
-    int64_t rows = 0;
-    int rc = validate(base, bias, blk, N, B, V, stride_base_r, stride_bias_r, &rows);
-    if (rc != XPRESS_OK || rows == 0) return rc;
+    return run_readout(base, bias, nullptr, blk, N, B, V, stride_base_r, stride_bias_r,
+                       stream);
+}
 
-    const Plan p = make_plan(base, bias, rows, V, stride_base_r, stride_bias_r);
-    RowArgs a;
-    a.base = base;
-    a.bias = bias;
-    a.blk = blk;
-    a.stride_base = stride_base_r;
-    a.stride_bias = stride_bias_r;
-    a.rows = (uint32_t)rows;
-    a.bm1 = (uint32_t)(B - 1);
-    a.V = (uint32_t)V;
-    a.splits = (uint32_t)p.splits;
-    a.keys = nullptr;
-
-    if (p.combine != kSingle) {
-        Workspace* w = nullptr;
-        const int64_t table = (p.combine == kTwoPass) ? rows * p.splits : 0;
-        const bool words = (p.combine == kAtomic || p.combine == kBalanced);
-        rc = ensure_workspace(stream, words ? rows : 0, table, &w);
-        if (rc != XPRESS_OK) return rc;
-        if (words) {
-            a.keys = w->keys;
-        } else {
-            a.keys = w->table;
-        }
-    }
-
-    hipError_t e = launch_plan(a, p, stream);
-    if (e != hipSuccess) return hip_fail(e);
-    if (p.combine == kTwoPass) {
-        const uint32_t grid = (uint32_t)((rows + 255) / 256 < 65536 ? (rows + 255) / 256 : 65536);
-        hipLaunchKernelGGL(reduce_keys_kernel, dim3(grid), dim3(256), 0, stream, a);
-        e = hipGetLastError();
-        if (e != hipSuccess) return hip_fail(e);
-    }
-    return XPRESS_OK;
+int xpress_topc_argmax_to_blk(const uint16_t* base_c, const uint16_t* bias_c,
+                              const int64_t* cand, int64_t* blk, int64_t N, int64_t B,
+                              int64_t C, hipStream_t stream)
+{
+    if (N > 0 && B > 1 && cand == nullptr) return XPRESS_EINVAL;
+    return run_readout(base_c, bias_c, cand, blk, N, B, C, C, C, stream);
 }
 
 int xpress_reserve(int64_t N, int64_t B, int64_t V, hipStream_t stream)

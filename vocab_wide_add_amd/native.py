@@ -57,6 +57,8 @@ def load():
         ip = ctypes.POINTER(ctypes.c_int)
         lib.xpress_add_argmax_to_blk.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, vp]
         lib.xpress_add_argmax_to_blk.restype = i32
+        lib.xpress_topc_argmax_to_blk.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
+        lib.xpress_topc_argmax_to_blk.restype = i32
         lib.xpress_reserve.argtypes = [i64, i64, i64, vp]
         lib.xpress_reserve.restype = i32
         lib.xpress_release.argtypes = []
@@ -118,6 +120,16 @@ def xpress_add_argmax_to_blk(base, bias, blk, N: int, B: int, V: int,
                                         int(V), int(stride_base_r), int(stride_bias_r),
                                         _stream(stream)),
            "xpress_add_argmax_to_blk")
+
+
+def xpress_topc_argmax_to_blk(base_c, bias_c, cand, blk, N: int, B: int, C: int,
+                              stream=None) -> None:
+    """blk[n, 1+j] = cand[r, argmax_c bf16(base_c[r, c] + bias_c[r, c])],
+    r = n*(B-1) + j; base_c, bias_c, cand are [N, B-1, C] contiguous."""
+    lib = load()
+    _check(lib.xpress_topc_argmax_to_blk(_ptr(base_c), _ptr(bias_c), _ptr(cand), _ptr(blk),
+                                         int(N), int(B), int(C), _stream(stream)),
+           "xpress_topc_argmax_to_blk")
 
 
 def xpress_reserve(N: int, B: int, V: int, stream=None) -> None:
