@@ -110,6 +110,36 @@ def copy_probe(nbytes: int, reps: int):
     print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}))
 
 
+def time_graph(step, steps: int, warmup: int, per_graph: int, reserve):
+    """Capture ``per_graph`` steps into one HIP graph and time ``steps``
+    steps as graph replays (region 1: wall clock and one HIP event pair
+    around the replays).  Returns (wall seconds, GPU seconds, None)."""
+    import torch
+    cap = torch.cuda.Stream()
+    reserve(cap)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        for k in range(per_graph):
+            step(k, cap)
+    reps = max(1, steps // per_graph)
+    for _ in range(max(1, warmup // per_graph)):
+        graph.replay()
+    torch.cuda.synchronize()
+    log("timing %d graph replays of %d steps" % (reps, per_graph))
+    r0 = torch.cuda.Event(enable_timing=True)
+    r1 = torch.cuda.Event(enable_timing=True)
+    cur = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    r0.record(cur)
+    for _ in range(reps):
+        graph.replay()
+    r1.record(cur)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, r0.elapsed_time(r1) * 1e-3, reps * per_graph
+
+
 def time_steps(step, steps: int, warmup: int, stream):
     """Warm up, then time ``steps`` calls twice: region 1 back to back (wall
     clock and one HIP event pair on the launch stream around the region),
@@ -198,16 +228,23 @@ def bench_readout(args, np, torch, native, workloads):
                                        w.stride_base, w.stride_bias)
     native.xpress_reserve(w.N, w.B, w.V, stream=stream)
 
-    def step(k):
+    def step(k, st=stream):
         b, i, blk = dev[k % sets]
         native.xpress_add_argmax_to_blk(b, i, blk, w.N, w.B, w.V, w.stride_base,
-                                        w.stride_bias, stream=stream)
+                                        w.stride_bias, stream=st)
 
-    wall, region_gpu, durs = time_steps(step, args.steps, args.warmup, stream)
+    if args.graph:
+        wall, region_gpu, n = time_graph(step, args.steps, args.warmup, args.graph,
+                                         lambda st: native.xpress_reserve(w.N, w.B, w.V, stream=st))
+        args.steps = n
+        durs = [region_gpu / n]
+    else:
+        wall, region_gpu, durs = time_steps(step, args.steps, args.warmup, stream)
     got = dev[(args.steps - 1) % sets][2].cpu().numpy()
     config = {"workload": name, "N": w.N, "B": w.B, "V": w.V, "rows": w.rows,
               "stride_base": w.stride_base, "stride_bias": w.stride_bias,
-              "bytes_per_step": w.bytes_read, "input_sets": sets, "plan": plan}
+              "bytes_per_step": w.bytes_read, "input_sets": sets, "plan": plan,
+              "launch": ("hip graph of %d steps" % args.graph) if args.graph else "stream"}
     out = result_line("effective HBM GB/s (+ %% of peak) and rows/s, add+argmax N=%d B=%d V=%d"
                       % (w.N, w.B, w.V), name, config, w.bytes_read, w.rows, args.steps,
                       args.warmup, wall, region_gpu, durs, plan["launches"], traffic_for(name))
@@ -241,13 +278,20 @@ def bench_topc(args, np, torch, native, workloads):
     plan = native.xpress_describe_plan(dev[0][0], dev[0][1], w.N, w.B, w.C, w.C, w.C)
     native.xpress_reserve(w.N, w.B, w.C, stream=stream)
 
-    def step(k):
+    def step(k, st=stream):
         b, i, c, blk = dev[k % sets]
-        native.xpress_topc_argmax_to_blk(b, i, c, blk, w.N, w.B, w.C, stream=stream)
+        native.xpress_topc_argmax_to_blk(b, i, c, blk, w.N, w.B, w.C, stream=st)
 
-    wall, region_gpu, durs = time_steps(step, args.steps, args.warmup, stream)
+    if args.graph:
+        wall, region_gpu, n = time_graph(step, args.steps, args.warmup, args.graph,
+                                         lambda st: native.xpress_reserve(w.N, w.B, w.C, stream=st))
+        args.steps = n
+        durs = [region_gpu / n]
+    else:
+        wall, region_gpu, durs = time_steps(step, args.steps, args.warmup, stream)
     config = {"workload": name, "op": "topc", "N": w.N, "B": w.B, "C": w.C, "rows": w.rows,
-              "bytes_per_step": w.bytes_read, "input_sets": sets, "plan": plan}
+              "bytes_per_step": w.bytes_read, "input_sets": sets, "plan": plan,
+              "launch": ("hip graph of %d steps" % args.graph) if args.graph else "stream"}
     out = result_line("top-C readout: effective GB/s and rows/s, N=%d B=%d C=%d"
                       % (w.N, w.B, w.C), name, config, w.bytes_read, w.rows, args.steps,
                       args.warmup, wall, region_gpu, durs, plan["launches"], None)
@@ -280,6 +324,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--op", choices=["readout", "topc"], default="readout")
+    ap.add_argument("--graph", type=int, default=0,
+                    help="capture this many steps per HIP graph and time graph replays")
     ap.add_argument("--topc-c", type=int, default=1024, choices=[64, 256, 1024, 4096])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU work budget of the oracle baseline leg")
