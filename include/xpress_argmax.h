@@ -103,8 +103,11 @@ int xpress_add_argmax_to_blk(const uint16_t* base, const uint16_t* bias,
  *   N, B            as above; C >= 1 candidates per row (<= 2^31 - 1).
  *   stream          HIP stream (0 = the null stream).
  *
- * Asynchronous; same plans, workspace, no-op and error rules as
- * xpress_add_argmax_to_blk (with V = C and row strides C).
+ * Asynchronous; same no-op and error rules as xpress_add_argmax_to_blk.
+ * With the automatic plan, lists of up to 256 candidates are read by one wave
+ * per row that carries the ids along (no second round trip for the gather);
+ * longer lists, or any plan set with xpress_set_plan, take the streaming
+ * readout with V = C and row strides C and gather the id when writing blk.
  */
 int xpress_topc_argmax_to_blk(const uint16_t* base_c, const uint16_t* bias_c,
                               const int64_t* cand, int64_t* blk, int64_t N,

@@ -122,3 +122,31 @@ def test_topc_invalid_arguments_raise():
         native.xpress_topc_argmax_to_blk(x, x, 0, blk, 1, 2, 8)
     with pytest.raises(native.XpressError):
         native.xpress_topc_argmax_to_blk(x, x, c, c, 1, 2, 8)  # blk aliases cand
+
+
+@pytest.mark.parametrize("C", [1, 2, 7, 8, 9, 63, 64, 65, 100, 1000, 4096, 4097])
+@pytest.mark.parametrize("offset", [0, 1])
+def test_topc_default_plan_ragged_and_unaligned(C, offset):
+    """The default top-C plan (one wave per row carrying the ids, up to 4096
+    candidates; the streaming readout above) on ragged counts, with aligned
+    buffers and with base_c / bias_c / cand shifted off 16-byte alignment."""
+    import torch
+    N, B = 7, 5
+    rows = N * (B - 1)
+    base_c, bias_c, cand = _rows(rows, C, 1000 + C)
+    blk0 = np.full((N, B), -1, dtype=np.int64)
+    blk0[:, 0] = 55
+    want = oracle_topc(base_c, bias_c, cand, blk0, N, B, C)
+    big_a = np.zeros(base_c.size + 8, np.uint16)
+    big_b = np.zeros(bias_c.size + 8, np.uint16)
+    big_c = np.zeros(cand.size + 2, np.int64)
+    big_a[offset:offset + base_c.size] = base_c.reshape(-1)
+    big_b[offset:offset + bias_c.size] = bias_c.reshape(-1)
+    big_c[offset:offset + cand.size] = cand.reshape(-1)
+    da, db, dc = to_dev(big_a), to_dev(big_b), to_dev(big_c)
+    blk_d = to_dev(blk0)
+    say("topc default plan C=%d offset=%d" % (C, offset))
+    native.xpress_topc_argmax_to_blk(da.data_ptr() + 2 * offset, db.data_ptr() + 2 * offset,
+                                     dc.data_ptr() + 8 * offset, blk_d, N, B, C)
+    torch.cuda.synchronize()
+    assert np.array_equal(blk_d.cpu().numpy(), want)
