@@ -70,6 +70,11 @@ def _load():
         lib.oracle_topc_argmax_to_blk.argtypes = [
             _U16P, _U16P, _I64P, _I64P] + [ctypes.c_int64] * 3
         lib.oracle_topc_argmax_to_blk.restype = ctypes.c_int
+        lib.oracle_dot_bf16.argtypes = [_U16P, _U16P, ctypes.c_int64]
+        lib.oracle_dot_bf16.restype = ctypes.c_uint16
+        lib.oracle_gemm_argmax_rows.argtypes = [
+            _U16P, _U16P, _U16P, _I64P] + [ctypes.c_int64] * 5
+        lib.oracle_gemm_argmax_rows.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -211,3 +216,50 @@ def topc_argmax_to_blk(base_c, bias_c, cand, blk: np.ndarray, N: int, B: int, C:
         N, B, C)
     if rc != 0:
         raise ValueError("oracle rejected the sizes")
+
+
+def dot_bf16(x_row, w_row) -> int:
+    """bf16 pattern of the dot product of two bf16 rows, rounded once."""
+    a = _u16(x_row).reshape(-1)
+    b = _u16(w_row).reshape(-1)
+    if a.size != b.size or a.size < 1:
+        raise ValueError("rows must be non-empty and of equal length")
+    return int(_load().oracle_dot_bf16(_p16(a), _p16(b), a.size))
+
+
+def gemm_argmax_rows(base, x, w, rows, V: int, R: int, stride_base_r: int,
+                     threads: int = 1) -> np.ndarray:
+    """First argmax of bf16(base + bf16(x @ w.T)) for each row listed in
+    ``rows`` (an iterable of row indices); base [.., stride], x [.., R] and
+    w [V, R] are uint16 bf16 patterns.  Rows are spread over host threads."""
+    base = _u16(base).reshape(-1)
+    x = _u16(x).reshape(-1)
+    w = _u16(w).reshape(-1)
+    rows = [int(r) for r in rows]
+    if w.size < V * R:
+        raise ValueError("w must hold V*R elements")
+    for r in rows:
+        if r < 0 or (r + 1) * R > x.size or r * stride_base_r + V > base.size:
+            raise ValueError("row %d outside the buffers" % r)
+    out = np.empty(len(rows), dtype=np.int64)
+    lib = _load()
+
+    def work(idx):
+        one = np.empty(1, dtype=np.int64)
+        for j in idx:
+            r = rows[j]
+            rc = lib.oracle_gemm_argmax_rows(_p16(base), _p16(x), _p16(w),
+                                             one.ctypes.data_as(_I64P), r, r + 1, V, R,
+                                             stride_base_r)
+            if rc != 0:
+                raise ValueError("oracle rejected the sizes")
+            out[j] = one[0]
+
+    threads = max(1, min(int(threads), len(rows) if rows else 1))
+    parts = [list(range(t, len(rows), threads)) for t in range(threads)]
+    ts = [threading.Thread(target=work, args=(p,)) for p in parts]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    return out

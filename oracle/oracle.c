@@ -237,3 +237,60 @@ int oracle_topc_argmax_to_blk(const uint16_t* base_c, const uint16_t* bias_c,
     }
     return 0;
 }
+
+/* ---------------------------------------------------------------------------
+ * Readout with the refiner bias computed in place (XPress kernels page,
+ * module description: logits = base + x @ W2, the readout matmul, followed by
+ * the argmax; the fused add + argmax consumes its bf16 result as bias):
+ *
+ *   bias[r, v] = bf16( sum_k x[r, k] * w[v, k] )      (the matmul's bf16 output)
+ *   s[r, v]    = bf16( base[r, v] + bias[r, v] )
+ *   blk[n, 1 + b] = first argmax_v s[r, v],   r = n*(B-1) + b
+ *
+ * x is [rows, R] and w is [V, R] (the head weight, one row per vocabulary id),
+ * both bf16 and row-major; base has row stride stride_base_r.  Reading: the
+ * dot product is the exact real sum rounded once to bf16 (the matmul
+ * accumulates in fp32 and rounds its output to bf16; the exact value is its
+ * plain definition).  Here each product of two bf16 values is exact in
+ * binary64 and the sum is formed in binary64, which is exact for the
+ * dyadic test inputs and within 2^-53 relative of the exact sum otherwise.
+ * ------------------------------------------------------------------------- */
+uint16_t oracle_dot_bf16(const uint16_t* x_row, const uint16_t* w_row, int64_t R)
+{
+    double acc = 0.0;
+    for (int64_t k = 0; k < R; ++k) {
+        acc += oracle_bf16_to_double(x_row[k]) * oracle_bf16_to_double(w_row[k]);
+    }
+    return oracle_bf16_from_double(acc);
+}
+
+/* First argmax of bf16(base + bf16(x_row . w[v])) over v = 0 .. V-1. */
+int64_t oracle_gemm_argmax_row(const uint16_t* base_row, const uint16_t* x_row,
+                               const uint16_t* w, int64_t V, int64_t R)
+{
+    int64_t best_v = 0;
+    double best = 0.0;
+    for (int64_t v = 0; v < V; ++v) {
+        uint16_t bias = oracle_dot_bf16(x_row, w + v * R, R);
+        double s = oracle_bf16_to_double(oracle_bf16_sum(base_row[v], bias));
+        if (v == 0 || s > best) {
+            best = s;
+            best_v = v;
+        }
+    }
+    return best_v;
+}
+
+/* Rows [r0, r1): idx_out[r - r0] = first argmax of row r. */
+int oracle_gemm_argmax_rows(const uint16_t* base, const uint16_t* x, const uint16_t* w,
+                            int64_t* idx_out, int64_t r0, int64_t r1, int64_t V,
+                            int64_t R, int64_t stride_base_r)
+{
+    if (r0 < 0 || r1 < r0 || V < 1 || R < 1 || stride_base_r < V) {
+        return -1;
+    }
+    for (int64_t r = r0; r < r1; ++r) {
+        idx_out[r - r0] = oracle_gemm_argmax_row(base + r * stride_base_r, x + r * R, w, V, R);
+    }
+    return 0;
+}

@@ -382,3 +382,74 @@ def test_topc_matches_torch_add_argmax_gather(name):
     ref = torch.gather(torch.from_numpy(cand), 1, pos[:, None])[:, 0].numpy()
     oracle.topc_argmax_to_blk(base_c, bias_c, cand, blk, w.N, w.B, w.C)
     assert np.array_equal(blk[:, 1:].reshape(-1), ref)
+
+
+def load_gemm_rows():
+    out = []
+    with open(os.path.join(GOLDEN, "gemm_rows.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, x, w, base, idx, why = [p.strip() for p in line.split(";", 5)]
+            x = np.array([int(t, 16) for t in x.split()], dtype=np.uint16)
+            w = np.array([[int(t, 16) for t in row.split()] for row in w.split("|")],
+                         dtype=np.uint16)
+            base = np.array([int(t, 16) for t in base.split()], dtype=np.uint16)
+            out.append((name, x, w, base, int(idx), why))
+    return out
+
+
+GEMM_ROWS = load_gemm_rows()
+
+
+@pytest.mark.parametrize("name,x,w,base,idx,why", GEMM_ROWS, ids=[c[0] for c in GEMM_ROWS])
+def test_gemm_golden(name, x, w, base, idx, why):
+    V, R = w.shape
+    got = oracle.gemm_argmax_rows(base, x, w, [0], V, R, V)
+    assert got[0] == idx, why
+
+
+def test_dot_bf16_exact_cases():
+    one, half, e8 = 0x3F80, 0x3F00, 0x3B80
+    assert oracle.dot_bf16(np.array([one, one], np.uint16), np.array([half, half], np.uint16)) == one
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: even (1) wins
+    assert oracle.dot_bf16(np.array([one, one], np.uint16), np.array([one, e8], np.uint16)) == one
+    # exact cancellation
+    assert oracle.dot_bf16(np.array([0x4000, 0xC000], np.uint16),
+                           np.array([one, one], np.uint16)) == 0x0000
+
+
+@pytest.mark.parametrize("name", ["gemm_tiny_n2_b4_v1000_r64", "gemm_small_n8_b8_v32000_r256"])
+def test_gemm_matches_torch_matmul_add_argmax(name):
+    """The unfused spelling on the CPU: the matmul in float64 (exact for the
+    dyadic inputs, so its float32 and bf16 roundings are single roundings of
+    the exact value), rounded to bf16, a bf16 add with base, argmax (first
+    occurrence) -- equals the oracle on every row checked."""
+    w = workloads.GEMM_WORKLOADS[name]
+    base, x, wt, _ = workloads.generate_gemm(w, rows_limit=min(w.rows, 12))
+    rows = base.shape[0]
+
+    def as_f64(b):
+        return torch.from_numpy((b.astype(np.uint32) << 16).view(np.float32)).double()
+
+    bias = (as_f64(x) @ as_f64(wt).T).float().to(torch.bfloat16)
+    b16 = torch.from_numpy(base.view(np.int16)).view(torch.bfloat16)
+    ref = torch.argmax(b16 + bias, dim=-1).numpy()
+    got = oracle.gemm_argmax_rows(base, x, wt, range(rows), w.V, w.R, w.V, threads=8)
+    assert np.array_equal(got, ref)
+
+
+def test_gemm_planted_closed_form():
+    """w row v = r mod V aligned with x row r by a large margin: that id wins."""
+    g = np.random.Generator(np.random.PCG64(4))
+    rows, V, R = 9, 50, 32
+    x = (g.integers(-8, 9, size=(rows, R)) / 8.0).astype(np.float32)
+    wt = (g.integers(-1, 2, size=(V, R)) / 64.0).astype(np.float32)
+    for r in range(rows):
+        wt[r % V] = np.sign(x[r]) * 1.0
+    x[np.abs(x) == 0] = 0.125
+    base = np.zeros((rows, V), np.float32)
+    got = oracle.gemm_argmax_rows(workloads.f32_to_bf16_bits(base), workloads.f32_to_bf16_bits(x),
+                                  workloads.f32_to_bf16_bits(wt), range(rows), V, R, V)
+    assert list(got) == [r % V for r in range(rows)]

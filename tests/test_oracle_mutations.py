@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import exact_bf16
-from test_oracle import ARGMAX_ROWS, ROUNDING, TOPC_ROWS
+from test_oracle import ARGMAX_ROWS, GEMM_ROWS, ROUNDING, TOPC_ROWS
 from vocab_wide_add_amd import workloads
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -44,6 +44,11 @@ MUTATIONS = {
                              "blk[n * B + 1 + j] = best;"),
     "topc_wrong_row": ("blk[n * B + 1 + j] = cand[r * C + best];",
                        "blk[n * B + 1 + j] = cand[best];"),
+    "gemm_bias_dropped": ("oracle_bf16_sum(base_row[v], bias)", "oracle_bf16_sum(base_row[v], 0)"),
+    "gemm_x_row_ignored": ("oracle_gemm_argmax_row(base + r * stride_base_r, x + r * R, w, V, R)",
+                           "oracle_gemm_argmax_row(base + r * stride_base_r, x, w, V, R)"),
+    "gemm_bias_unrounded": ("return oracle_bf16_from_double(acc);",
+                            "return oracle_bf16_from_double(acc) | 1;"),
 }
 
 
@@ -65,6 +70,8 @@ def _build_mutant(tmp_path, name):
     lib.oracle_add_argmax_to_blk.restype = ctypes.c_int
     lib.oracle_topc_argmax_to_blk.argtypes = [U16P, U16P, I64P, I64P] + [ctypes.c_int64] * 3
     lib.oracle_topc_argmax_to_blk.restype = ctypes.c_int
+    lib.oracle_gemm_argmax_rows.argtypes = [U16P, U16P, U16P, I64P] + [ctypes.c_int64] * 5
+    lib.oracle_gemm_argmax_rows.restype = ctypes.c_int
     return lib
 
 
@@ -113,6 +120,24 @@ def _pins_pass(lib) -> bool:
                                   cand.ctypes.data_as(I64P), blk.ctypes.data_as(I64P), 1, 3, 2)
     if list(blk[0]) != [-1, 11, 20]:
         return False
+    for _, x, w, base, idx, _ in GEMM_ROWS:
+        V, R = w.shape
+        out = np.empty(1, dtype=np.int64)
+        x, w, base = (np.ascontiguousarray(t) for t in (x, w, base))
+        lib.oracle_gemm_argmax_rows(base.ctypes.data_as(U16P), x.ctypes.data_as(U16P),
+                                    w.ctypes.data_as(U16P), out.ctypes.data_as(I64P),
+                                    0, 1, V, R, V)
+        if out[0] != idx:
+            return False
+    # two rows whose x differ: row 1 must use its own x
+    x = np.array([0x3F80, 0x0000, 0x0000, 0x3F80], dtype=np.uint16)      # [[1,0],[0,1]]
+    w = np.array([0x3F80, 0x0000, 0x0000, 0x3F80], dtype=np.uint16)      # [[1,0],[0,1]]
+    base = np.zeros(4, dtype=np.uint16)
+    out = np.empty(2, dtype=np.int64)
+    lib.oracle_gemm_argmax_rows(base.ctypes.data_as(U16P), x.ctypes.data_as(U16P),
+                                w.ctypes.data_as(U16P), out.ctypes.data_as(I64P), 0, 2, 2, 2, 2)
+    if list(out) != [0, 1]:
+        return False
     return True
 
 
@@ -133,6 +158,8 @@ def test_unmutated_oracle_passes_the_pins(tmp_path):
     lib.oracle_add_argmax_to_blk.restype = ctypes.c_int
     lib.oracle_topc_argmax_to_blk.argtypes = [U16P, U16P, I64P, I64P] + [ctypes.c_int64] * 3
     lib.oracle_topc_argmax_to_blk.restype = ctypes.c_int
+    lib.oracle_gemm_argmax_rows.argtypes = [U16P, U16P, U16P, I64P] + [ctypes.c_int64] * 5
+    lib.oracle_gemm_argmax_rows.restype = ctypes.c_int
     assert _pins_pass(lib)
 
 

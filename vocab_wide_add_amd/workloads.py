@@ -245,3 +245,78 @@ def generate_topc(w: TopCWorkload):
     blk = np.full((w.N, w.B), -1, dtype=np.int64)
     blk[:, 0] = gi.integers(0, V, size=w.N)
     return f32_to_bf16_bits(base_c), f32_to_bf16_bits(bias_c), cand, blk
+
+
+# ---------------------------------------------------------------------------
+# Readout with the bias computed in place: base [rows, V], the refiner
+# latent x [rows, R] and the head weight w [V, R], all bf16.
+# ---------------------------------------------------------------------------
+
+
+@dataclasses.dataclass(frozen=True)
+class GemmWorkload:
+    name: str
+    N: int
+    B: int
+    V: int
+    R: int
+    seed: int
+    dyadic: bool  # x, w on the grid k/8, |k| <= 8: every fp32 partial sum is exact
+
+    @property
+    def rows(self) -> int:
+        return self.N * (self.B - 1)
+
+    @property
+    def bytes_read(self) -> int:
+        """Algorithmic HBM bytes of one call: base (2 B per logit) and the
+        head weight (2 B per element, read once); x is 2*rows*R."""
+        return self.rows * self.V * 2 + self.V * self.R * 2 + self.rows * self.R * 2
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.rows * self.V * self.R
+
+
+GEMM_WORKLOADS = {
+    w.name: w
+    for w in [
+        GemmWorkload("gemm_tiny_n2_b4_v1000_r64", 2, 4, 1000, 64, 20, True),
+        GemmWorkload("gemm_small_n8_b8_v32000_r256", 8, 8, 32000, 256, 21, True),
+        GemmWorkload("gemm_dyadic_n32_b16_v152064_r256", 32, 16, 152064, 256, 22, True),
+        GemmWorkload("gemm_normal_n32_b16_v152064_r256", 32, 16, 152064, 256, 23, False),
+    ]
+}
+
+GEMM_BENCH_WORKLOAD = "gemm_normal_n32_b16_v152064_r256"
+
+
+def generate_gemm(w: GemmWorkload, rows_limit: Optional[int] = None):
+    """Inputs of the readout with in-place bias.
+
+    Recipe (``SeedSequence(seed).spawn(4)``: base, x, w and id streams):
+    base ~ N(0, 4^2) in float32 rounded to bf16, [rows, V]; for the dyadic
+    workloads x and w are integers uniform on [-8, 8] divided by 8 (exact in
+    bf16; every product is a multiple of 1/64 of magnitude <= 1, so any fp32
+    partial sum over R <= 4096 terms is exact and the bias is order-free);
+    otherwise x ~ N(0, 1) and w ~ N(0, 1/R) (the bias is then ~N(0, 1)).
+    Anchors uniform on [0, V).  Returns ``(base, x, w, blk)`` as uint16 bf16
+    patterns ([rows, V], [rows, R], [V, R]) and int64 blk with draft slots
+    at -1.  ``rows_limit`` draws only the first rows of base and x.
+    """
+    s_base, s_x, s_w, s_ids = np.random.SeedSequence(w.seed).spawn(4)
+    keep = w.rows if rows_limit is None else min(w.rows, rows_limit)
+    gb = np.random.Generator(np.random.PCG64(s_base))
+    base = gb.standard_normal((keep, w.V), dtype=np.float32) * np.float32(4.0)
+    gx = np.random.Generator(np.random.PCG64(s_x))
+    gw = np.random.Generator(np.random.PCG64(s_w))
+    if w.dyadic:
+        x = gx.integers(-8, 9, size=(keep, w.R)).astype(np.float32) / np.float32(8.0)
+        wt = gw.integers(-8, 9, size=(w.V, w.R)).astype(np.float32) / np.float32(8.0)
+    else:
+        x = gx.standard_normal((keep, w.R), dtype=np.float32)
+        wt = gw.standard_normal((w.V, w.R), dtype=np.float32) * np.float32(1.0 / np.sqrt(w.R))
+    gi = np.random.Generator(np.random.PCG64(s_ids))
+    blk = np.full((w.N, w.B), -1, dtype=np.int64)
+    blk[:, 0] = gi.integers(0, w.V, size=w.N)
+    return f32_to_bf16_bits(base), f32_to_bf16_bits(x), f32_to_bf16_bits(wt), blk
