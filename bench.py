@@ -317,13 +317,74 @@ def bench_topc(args, np, torch, native, workloads):
     return out
 
 
+def bench_gemm(args, np, torch, native, workloads):
+    name = args.workload if (args.workload or "").startswith("gemm_") else workloads.GEMM_BENCH_WORKLOAD
+    w = workloads.GEMM_WORKLOADS[name]
+    log("generating %s" % name)
+    base, x, wt, blk0 = workloads.generate_gemm(w)
+    footprint = base.nbytes + x.nbytes + wt.nbytes
+    sets = max(1, math.ceil(2 * LLC_BYTES / footprint) + 1)
+    log("uploading %d input sets of %.1f MB" % (sets, footprint / 1e6))
+    cpu = [torch.from_numpy(t.view(np.int16)) for t in (base, x, wt)]
+    dev = [tuple(t.cuda() for t in cpu) + (torch.from_numpy(blk0).cuda(),) for _ in range(sets)]
+    stream = torch.cuda.current_stream()
+
+    def step(k, st=stream):
+        b, xx, ww, blk = dev[k % sets]
+        native.xpress_readout_gemm_argmax_to_blk(b, xx, ww, blk, w.N, w.B, w.V, w.R, w.V,
+                                                 stream=st)
+
+    wall, region_gpu, durs = time_steps(step, args.steps, args.warmup, stream)
+    config = {"workload": name, "op": "readout_gemm", "N": w.N, "B": w.B, "V": w.V, "R": w.R,
+              "rows": w.rows, "bytes_per_step": w.bytes_read, "flops_per_step": w.flops,
+              "input_sets": sets}
+    out = result_line("readout with in-place bias (x @ w.T): effective GB/s and rows/s, "
+                      "N=%d B=%d V=%d R=%d" % (w.N, w.B, w.V, w.R), name, config, w.bytes_read,
+                      w.rows, args.steps, args.warmup, wall, region_gpu, durs, 2, None)
+    out["tflops"] = round(w.flops * args.steps / wall / 1e12, 2)
+
+    # context: the unfused path -- a library matmul writing the bf16 bias,
+    # then this library's readout over base and that bias
+    # (the weight is transposed once into a contiguous [R, V] copy: the library
+    # matmul then sees no transposed view)
+    bias = [torch.empty((w.rows, w.V), dtype=torch.bfloat16, device="cuda")]
+    w_t = [d[2].view(torch.bfloat16).t().contiguous() for d in dev]
+
+    def unfused(k, st=stream):
+        b, xx, ww, blk = dev[k % sets]
+        torch.matmul(xx.view(torch.bfloat16), w_t[k % sets], out=bias[0])
+        native.xpress_add_argmax_to_blk(b, bias[0].view(torch.int16), blk, w.N, w.B, w.V, w.V,
+                                        w.V, stream=st)
+
+    uw, ug, _ = time_steps(unfused, max(50, args.steps // 5), max(20, args.warmup // 5), stream)
+    out["unfused_us_per_step"] = round(ug / max(50, args.steps // 5) * 1e6, 2)
+    if not args.no_cpu_baseline:
+        import oracle
+        log("cpu baseline")
+        got = dev[(args.steps - 1) % sets][3].cpu().numpy()[:, 1:].reshape(-1)
+        cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else 1
+        n = max(cores, 16)
+        rows = list(range(0, w.rows, max(1, w.rows // n)))[:n]
+        t0 = time.perf_counter()
+        ans = oracle.gemm_argmax_rows(base, x, wt, rows, w.V, w.R, w.V, threads=cores)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(len(rows) * (w.V * 2 + w.R * 2) / dt / 1e9, 4),
+                               "unit": "GB/s", "cores": cores, "kind": "oracle",
+                               "rows_per_s": round(len(rows) / dt, 2),
+                               "sample": "%d of %d rows of %s, %.1f s on %d threads"
+                                         % (len(rows), w.rows, name, dt, cores)}
+        out["checked_rows"] = len(rows)
+        out["checked_equal_rows"] = int(np.sum(got[rows] == ans))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--op", choices=["readout", "topc"], default="readout")
+    ap.add_argument("--op", choices=["readout", "topc", "gemm"], default="readout")
     ap.add_argument("--graph", type=int, default=0,
                     help="capture this many steps per HIP graph and time graph replays")
     ap.add_argument("--topc-c", type=int, default=1024, choices=[64, 256, 1024, 4096])
@@ -352,6 +413,8 @@ def main():
         return
     if args.op == "topc":
         out = bench_topc(args, np, torch, native, workloads)
+    elif args.op == "gemm":
+        out = bench_gemm(args, np, torch, native, workloads)
     else:
         out = bench_readout(args, np, torch, native, workloads)
     print(json.dumps(out))

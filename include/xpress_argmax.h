@@ -114,6 +114,40 @@ int xpress_topc_argmax_to_blk(const uint16_t* base_c, const uint16_t* bias_c,
                               int64_t B, int64_t C, hipStream_t stream);
 
 /*
+ * xpress_readout_gemm_argmax_to_blk -- the readout with the refiner bias
+ * computed in place (XPress kernels page, module description: a pass forms
+ * logits = base + x @ W2 with a readout matmul and then takes the argmax; the
+ * fused add + argmax consumes the matmul's bf16 result as its bias).  Here
+ * the matmul runs on the matrix cores inside the readout and neither the
+ * bias nor the logits are ever written:
+ *
+ *     bias[r, v]    = bf16( sum_k x[r, k] * w[v, k] )   (fp32 accumulation,
+ *                                                         rounded once)
+ *     blk[n, 1 + b] = first argmax_v bf16( base[r, v] + bias[r, v] )
+ *
+ *   base           device pointer, bf16 [N*(B-1), V] with row stride
+ *                  stride_base_r (elements, >= V, a multiple of 8).
+ *   x              device pointer, bf16 [N*(B-1), R] row-major (the latent
+ *                  rows the refiner produced for the draft slots).
+ *   w              device pointer, bf16 [V, R] row-major (the readout
+ *                  weight, one row per vocabulary id; W2 = w^T).
+ *   blk            device pointer to int64 [N, B]; slots 1..B-1 written.
+ *   N, B, V        as for xpress_add_argmax_to_blk.
+ *   R              latent width: 64, 128 or 256.
+ *   stream         HIP stream (0 = the null stream).
+ *
+ * base, x and w must be 16-byte aligned (XPRESS_EINVAL otherwise).  The fp32
+ * accumulation order is the matrix cores'; where every partial sum of the
+ * dot products is exact (e.g. inputs on a coarse dyadic grid) the result is
+ * bit-identical to rounding the exact dot product.  Asynchronous; two
+ * launches; uses the (device, stream) workspace (rows x ranges keys).
+ */
+int xpress_readout_gemm_argmax_to_blk(const uint16_t* base, const uint16_t* x,
+                                      const uint16_t* w, int64_t* blk, int64_t N,
+                                      int64_t B, int64_t V, int64_t R,
+                                      int64_t stride_base_r, hipStream_t stream);
+
+/*
  * xpress_reserve -- pre-allocate the workspace the readout would use for
  * (N, B, V) on `stream`'s device and stream, so that a later call -- e.g.
  * one being captured into a HIP graph -- allocates nothing.  Synchronous.

@@ -136,3 +136,26 @@ def test_topc_no_rows_is_ok_without_pointers():
     lib = native.load()
     assert lib.xpress_topc_argmax_to_blk(0, 0, 0, 0, 0, 16, 256, None) == 0
     assert lib.xpress_topc_argmax_to_blk(0, 0, 0, 0, 32, 1, 256, None) == 0
+
+
+@no_gpu_only
+@pytest.mark.parametrize("args", [
+    (256, 512, 1024, 4096, 1, 2, 8, 96, 8),     # R not 64/128/256
+    (258, 512, 1024, 4096, 1, 2, 8, 64, 8),     # base not 16-byte aligned
+    (256, 520, 1024, 4096, 1, 2, 8, 64, 8),     # x not 16-byte aligned
+    (256, 512, 1032, 4096, 1, 2, 8, 64, 8),     # w not 16-byte aligned
+    (256, 512, 1024, 4096, 1, 2, 8, 64, 12),    # stride not a multiple of 8
+    (256, 512, 1024, 4096, 1, 2, 8, 64, 4),     # stride < V
+    (256, 512, 1024, 520, 1, 2, 8, 64, 8),      # blk [520, 536) overlaps x [512, 640)
+    (0, 512, 1024, 4096, 1, 2, 8, 64, 8),       # null base
+])
+def test_gemm_invalid_arguments_rejected_before_launch(args):
+    lib = native.load()
+    assert lib.xpress_readout_gemm_argmax_to_blk(*args, None) == native.XPRESS_EINVAL
+
+
+@no_gpu_only
+def test_gemm_no_rows_is_ok_without_pointers():
+    lib = native.load()
+    assert lib.xpress_readout_gemm_argmax_to_blk(0, 0, 0, 0, 0, 16, 152064, 256, 152064,
+                                                 None) == 0

@@ -1,0 +1,155 @@
+"""Parity of the HIP readout-with-matmul (xpress_readout_gemm_argmax_to_blk)
+with the CPU oracle.
+
+Dyadic inputs (x, w on the grid k/8): every fp32 partial sum of the dot
+products is exact, so the GPU's bias equals the bf16 of the exact dot product
+whatever the matrix cores' accumulation order, and blk must match the oracle
+bit for bit.  N(0, 1) inputs: fp32 accumulation can move a bias across a bf16
+rounding boundary; the bias is then off by one bf16 ulp and the sum by at
+most two (one for the bias, one for the second rounding), so the GPU's winner
+must score within two bf16 ulps of the true maximum under the oracle's exact
+definition, and most rows must match exactly.
+"""
+import numpy as np
+import pytest
+
+from conftest import gpu_available
+from gpu_util import say, to_dev, ORACLE_THREADS
+import oracle
+from vocab_wide_add_amd import native, workloads
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+def gpu_gemm(base_d, x_d, w_d, blk0, N, B, V, R, S):
+    import torch
+    blk_d = to_dev(blk0)
+    native.xpress_readout_gemm_argmax_to_blk(base_d, x_d, w_d, blk_d, N, B, V, R, S)
+    torch.cuda.synchronize()
+    return blk_d.cpu().numpy()
+
+
+def sample_rows(rows, k=24):
+    picks = {0, 1, 31, 32, 33, 63, 64, rows - 1, rows - 2, rows // 2}
+    g = np.random.Generator(np.random.PCG64(rows))
+    picks |= set(int(r) for r in g.integers(0, rows, size=k))
+    return sorted(r for r in picks if 0 <= r < rows)
+
+
+@pytest.mark.parametrize("name", ["gemm_tiny_n2_b4_v1000_r64", "gemm_small_n8_b8_v32000_r256"])
+def test_gemm_small_workloads_every_row(name):
+    w = workloads.GEMM_WORKLOADS[name]
+    base, x, wt, blk0 = workloads.generate_gemm(w)
+    want = blk0.copy()
+    want[:, 1:] = oracle.gemm_argmax_rows(base, x, wt, range(w.rows), w.V, w.R, w.V,
+                                          threads=ORACLE_THREADS).reshape(w.N, w.B - 1)
+    say("gemm %s" % name)
+    got = gpu_gemm(to_dev(base), to_dev(x), to_dev(wt), blk0, w.N, w.B, w.V, w.R, w.V)
+    assert np.array_equal(got, want)
+
+
+def test_gemm_full_size_dyadic_sampled_rows():
+    w = workloads.GEMM_WORKLOADS["gemm_dyadic_n32_b16_v152064_r256"]
+    base, x, wt, blk0 = workloads.generate_gemm(w)
+    say("gemm full-size dyadic")
+    got = gpu_gemm(to_dev(base), to_dev(x), to_dev(wt), blk0, w.N, w.B, w.V, w.R, w.V)
+    assert np.array_equal(got[:, 0], blk0[:, 0])
+    flat = got[:, 1:].reshape(-1)
+    assert ((flat >= 0) & (flat < w.V)).all()
+    rows = sample_rows(w.rows)
+    want = oracle.gemm_argmax_rows(base, x, wt, rows, w.V, w.R, w.V, threads=ORACLE_THREADS)
+    assert np.array_equal(flat[rows], want)
+
+
+def _score(base, x, wt, r, v, V, R):
+    """bf16(base[r, v] + bf16(x[r] . w[v])) under the oracle's definition."""
+    bias = oracle.dot_bf16(x[r], wt[v])
+    return oracle.bf16_to_double(oracle.bf16_sum(int(base[r, v]), bias))
+
+
+def test_gemm_full_size_normal_within_derived_bound():
+    w = workloads.GEMM_WORKLOADS["gemm_normal_n32_b16_v152064_r256"]
+    base, x, wt, blk0 = workloads.generate_gemm(w)
+    say("gemm full-size N(0,1)")
+    got = gpu_gemm(to_dev(base), to_dev(x), to_dev(wt), blk0, w.N, w.B, w.V, w.R, w.V)
+    flat = got[:, 1:].reshape(-1)
+    assert ((flat >= 0) & (flat < w.V)).all()
+    rows = sample_rows(w.rows, k=40)
+    want = oracle.gemm_argmax_rows(base, x, wt, rows, w.V, w.R, w.V, threads=ORACLE_THREADS)
+    exact = 0
+    for r, vo in zip(rows, want):
+        vg = int(flat[r])
+        if vg == vo:
+            exact += 1
+            continue
+        s_best = _score(base, x, wt, r, int(vo), w.V, w.R)
+        s_gpu = _score(base, x, wt, r, vg, w.V, w.R)
+        ulp = 2.0 ** (np.floor(np.log2(abs(s_best))) - 7) if s_best != 0 else 2.0 ** -133
+        assert s_gpu >= s_best - 2 * ulp, (r, vg, vo, s_gpu, s_best)
+    assert exact >= 0.9 * len(rows)
+
+
+def _dyadic(rows, V, R, seed, pad=0):
+    g = np.random.Generator(np.random.PCG64(seed))
+    base = workloads.f32_to_bf16_bits(
+        (g.integers(-16, 17, size=(rows, V)) / 4.0).astype(np.float32))
+    if pad:
+        b = np.full((rows, V + pad), 0x42C8, np.uint16)
+        b[:, :V] = base
+        base = b
+    x = workloads.f32_to_bf16_bits((g.integers(-8, 9, size=(rows, R)) / 8.0).astype(np.float32))
+    wt = workloads.f32_to_bf16_bits((g.integers(-8, 9, size=(V, R)) / 8.0).astype(np.float32))
+    return base, x, wt
+
+
+@pytest.mark.parametrize("R", [64, 128, 256])
+@pytest.mark.parametrize("N,B,V", [(1, 2, 1), (1, 2, 63), (1, 33, 64), (3, 12, 65),
+                                   (2, 17, 1000), (5, 21, 4097), (1, 2, 130)])
+def test_gemm_ragged_shapes(R, N, B, V):
+    rows = N * (B - 1)
+    pad = (-V) % 8 + (8 if V % 3 == 0 else 0)   # strides a multiple of 8, sometimes padded
+    S = V + pad
+    base, x, wt = _dyadic(rows, V, R, seed=V * 7 + R + rows, pad=pad)
+    blk0 = np.full((N, B), -1, dtype=np.int64)
+    blk0[:, 0] = 3
+    want = blk0.copy()
+    want[:, 1:] = oracle.gemm_argmax_rows(base, x, wt, range(rows), V, R, S,
+                                          threads=ORACLE_THREADS).reshape(N, B - 1)
+    say("gemm ragged N=%d B=%d V=%d R=%d" % (N, B, V, R))
+    got = gpu_gemm(to_dev(base), to_dev(x), to_dev(wt), blk0, N, B, V, R, S)
+    assert np.array_equal(got, want)
+
+
+def test_gemm_repeated_calls_and_guard_cells():
+    import torch
+    N, B, V, R = 4, 16, 20000, 128
+    rows = N * (B - 1)
+    guard = 0x7E7E7E7E7E7E7E7E
+    for seed in range(3):
+        base, x, wt = _dyadic(rows, V, R, seed=100 + seed)
+        blk0 = np.full((N, B), -1, dtype=np.int64)
+        blk0[:, 0] = 9
+        want = blk0.copy()
+        want[:, 1:] = oracle.gemm_argmax_rows(base, x, wt, range(rows), V, R, V,
+                                              threads=ORACLE_THREADS).reshape(N, B - 1)
+        buf = np.full(N * B + 64, guard, dtype=np.int64)
+        buf[32:32 + N * B] = blk0.reshape(-1)
+        buf_d = to_dev(buf)
+        say("gemm guard cells seed=%d" % seed)
+        native.xpress_readout_gemm_argmax_to_blk(to_dev(base), to_dev(x), to_dev(wt),
+                                                 buf_d.data_ptr() + 32 * 8, N, B, V, R, V)
+        torch.cuda.synchronize()
+        out = buf_d.cpu().numpy()
+        assert (out[:32] == guard).all() and (out[32 + N * B:] == guard).all()
+        assert np.array_equal(out[32:32 + N * B].reshape(N, B), want)
+
+
+def test_gemm_invalid_arguments_raise():
+    import torch
+    b = torch.zeros(4096, dtype=torch.int16, device="cuda")
+    blk = torch.zeros(64, dtype=torch.int64, device="cuda")
+    with pytest.raises(native.XpressError):   # R unsupported
+        native.xpress_readout_gemm_argmax_to_blk(b, b, b, blk, 1, 2, 8, 96, 8)
+    with pytest.raises(native.XpressError):   # misaligned x
+        native.xpress_readout_gemm_argmax_to_blk(b, b.data_ptr() + 2, b, blk, 1, 2, 8, 64, 8)

@@ -10,7 +10,8 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "xpress_argmax.hip")
+SRCS = [os.path.join(PKG, "csrc", "xpress_argmax.hip"),
+        os.path.join(PKG, "csrc", "readout_gemm.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libxpress_argmax.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -34,7 +35,7 @@ FLAGS = [
 def build(verbose: bool = False) -> str:
     """Compile the library and return its path (always recompiles)."""
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + ["-I", INCLUDE, "-o", tmp, SRC]
+    cmd = [HIPCC] + FLAGS + ["-I", INCLUDE, "-o", tmp] + SRCS
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -1,0 +1,294 @@
+// readout_gemm.hip -- readout with the refiner bias computed in place, for
+// MI355X (gfx950).
+//
+// One Jacobi pass (XPress kernels page, module description) forms
+//     logits[r, v] = base[r, v] + (x @ W2)[r, v]
+// with a readout matmul whose bf16 result the fused add + argmax then
+// consumes as its bias.  Here that matmul is fused into the readout: the
+// bias tile comes out of the matrix cores, is rounded to bf16 exactly as the
+// matmul's bf16 output would be, added to base and rounded again, and only
+// the running first maximum of each row leaves the registers.  Neither the
+// [rows, V] bias nor the [rows, V] logits is ever written:
+//     bias[r, v]    = bf16( sum_k x[r, k] * w[v, k] )   (fp32 accumulation)
+//     s[r, v]       = bf16( base[r, v] + bias[r, v] )
+//     blk[n, 1 + b] = first argmax_v s[r, v],   r = n*(B-1) + b
+// x is [rows, R] and w is [V, R] (the head weight, one row per id), both bf16.
+//
+// Design (gfx950, wave64, v_mfma_f32_32x32x16_bf16):
+//   * the vocabulary runs along the MFMA's M dimension (A operand = a 32-id
+//     slice of w), the draft rows along N (B operand = x^T): each lane's 16
+//     accumulators are then 4 runs of 4 consecutive ids of ONE draft row,
+//     which is what the epilogue's running maximum wants;
+//   * a wave owns 32 draft rows; their x rows (R bf16 each) stay in
+//     registers as the B operands for the whole launch;
+//   * a workgroup of kWaves waves covers 32*kWaves rows and a contiguous range
+//     of 64-id tiles; each tile of w is staged through registers into a
+//     padded, double-buffered LDS tile shared by the waves, the next tile's
+//     loads in flight while the current one is multiplied;
+//   * the workgroups that cover the row groups of one vocabulary range are
+//     placed on one XCD (workgroup b runs on XCD b mod 8), so each w tile is
+//     fetched from HBM once and served from that XCD's L2 afterwards;
+//   * per (row, range) the packed (value, ~id) key goes to a key table and the
+//     library's second pass reduces each row's keys into blk.
+// Numerics: the fp32 accumulation order of the MFMA is the hardware's; where
+// every partial sum is exact (dyadic inputs) the bias equals the bf16 of the
+// exact dot product bit for bit.
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "xpress_argmax.h"
+#include "device_common.h"
+#include "host_common.h"
+
+namespace {
+
+using namespace xpress;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kTileV = 64;   // vocabulary ids per tile: two 32-id MFMA slices
+constexpr int kWaves = 4;    // waves (32-row groups) per workgroup
+
+struct GemmArgs {
+    const uint16_t* base;
+    const uint16_t* x;
+    const uint16_t* w;
+    uint64_t* table;       // [rows, ranges] packed keys
+    int64_t stride_base;   // elements
+    uint32_t rows;
+    uint32_t V;
+    uint32_t tiles;        // ceil(V / kTileV)
+    uint32_t ranges;       // vocabulary ranges (a multiple of 8)
+    uint32_t row_wgs;      // workgroups per range (row groups / kWaves)
+};
+
+// Two fp32 values rounded to bf16 (round-to-nearest-even), packed lo | hi.
+__device__ __forceinline__ uint32_t round_pack2(float lo, float hi)
+{
+    f32x2 s;
+    s.x = lo;
+    s.y = hi;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(s, bf16x2));
+}
+
+template <int R>
+__global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
+{
+    constexpr int KC = R / 16;                  // MFMA steps over k
+    constexpr int ROWB = R * 2 + 16;            // bytes per LDS tile row (16 B pad)
+    constexpr int CHUNKS = kTileV * R / 8;      // 16-byte chunks per w tile
+    constexpr int THREADS = kWaves * 64;
+    constexpr int PER_THREAD = CHUNKS / THREADS;
+    static_assert(CHUNKS % THREADS == 0, "tile must split evenly over the workgroup");
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2][kTileV * ROWB];
+
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = threadIdx.x >> 6;
+    const uint32_t khalf = lane >> 5;
+    const uint32_t b = blockIdx.x;
+    const uint32_t xcd = b & 7u;
+    const uint32_t local = b >> 3;
+    const uint32_t range = (local / a.row_wgs) * 8u + xcd;
+    const uint32_t rw = local % a.row_wgs;
+    const uint32_t t0 = (uint32_t)((uint64_t)range * a.tiles / a.ranges);
+    const uint32_t t1 = (uint32_t)((uint64_t)(range + 1u) * a.tiles / a.ranges);
+
+    const uint32_t row = (rw * kWaves + wave) * 32u + (lane & 31u);
+    const bool row_ok = row < a.rows;
+
+    // B operands: this lane's draft row of x, 8 of the 16 k of every step
+    bf16x8 bx[KC];
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (row_ok) {
+            v = *reinterpret_cast<const u32x4*>(a.x + (uint64_t)row * R + 16 * c + 8 * khalf);
+        }
+        bx[c] = __builtin_bit_cast(bf16x8, v);
+    }
+
+    // staging of one w tile: chunk id -> (tile row, 16-byte column)
+    u32x4 stage[PER_THREAD];
+    auto load_tile = [&](uint32_t t) {
+#pragma unroll
+        for (int i = 0; i < PER_THREAD; ++i) {
+            const uint32_t id = threadIdx.x + i * THREADS;
+            const uint32_t trow = id / (R / 8);
+            const uint32_t tcol = id % (R / 8);
+            const uint32_t v = t * kTileV + trow;
+            u32x4 val = {0u, 0u, 0u, 0u};
+            if (v < a.V) {
+                val = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4*>(a.w + (uint64_t)v * R) + tcol);
+            }
+            stage[i] = val;
+        }
+    };
+    auto store_tile = [&](uint32_t buf) {
+#pragma unroll
+        for (int i = 0; i < PER_THREAD; ++i) {
+            const uint32_t id = threadIdx.x + i * THREADS;
+            const uint32_t trow = id / (R / 8);
+            const uint32_t tcol = id % (R / 8);
+            *reinterpret_cast<u32x4*>(&lds[buf][trow * ROWB + tcol * 16]) = stage[i];
+        }
+    };
+
+    float best = -__builtin_inff();
+    uint32_t bidx = kNoIndex;
+
+    if (t0 < t1) {
+        load_tile(t0);
+        store_tile(0);
+    }
+    __syncthreads();
+
+    for (uint32_t t = t0; t < t1; ++t) {
+        const uint32_t cur = (t - t0) & 1u;
+        const bool more = t + 1u < t1;
+        if (more) load_tile(t + 1u);
+
+        // base for this tile: per slice g and run q, 4 consecutive ids
+        u32x2 bv[2][4];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t v = t * kTileV + 32u * g + 8u * q + 4u * khalf;
+                u32x2 val = {0u, 0u};
+                if (row_ok) {
+                    const uint16_t* p = a.base + (int64_t)row * a.stride_base + v;
+                    if (v + 3u < a.V) {
+                        val = *reinterpret_cast<const u32x2*>(p);
+                    } else {
+                        uint16_t e[4] = {0, 0, 0, 0};
+                        for (uint32_t j = 0; j < 4u; ++j) {
+                            if (v + j < a.V) e[j] = p[j];
+                        }
+                        val.x = (uint32_t)e[0] | ((uint32_t)e[1] << 16);
+                        val.y = (uint32_t)e[2] | ((uint32_t)e[3] << 16);
+                    }
+                }
+                bv[g][q] = val;
+            }
+        }
+
+        f32x16 acc[2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            acc[g] = f32x16{};
+            const unsigned char* arow = &lds[cur][(32u * g + (lane & 31u)) * ROWB + 16u * khalf];
+#pragma unroll
+            for (int c = 0; c < KC; ++c) {
+                const bf16x8 av =
+                    __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(arow + 32 * c));
+                acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bx[c], acc[g], 0, 0, 0);
+            }
+        }
+
+        // epilogue: bias rounded to bf16, added to base, rounded; ascending ids
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t v = t * kTileV + 32u * g + 8u * q + 4u * khalf;
+                const uint32_t s01 = add_round2(bv[g][q].x,
+                                                round_pack2(acc[g][4 * q], acc[g][4 * q + 1]));
+                const uint32_t s23 = add_round2(bv[g][q].y,
+                                                round_pack2(acc[g][4 * q + 2], acc[g][4 * q + 3]));
+                const float sv[4] = {bf16_lo(s01), bf16_hi(s01), bf16_lo(s23), bf16_hi(s23)};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bool ok = row_ok && (v + j < a.V);
+                    const bool take = ok && ((sv[j] > best) | (bidx == kNoIndex));
+                    best = take ? sv[j] : best;
+                    bidx = take ? v + j : bidx;
+                }
+            }
+        }
+
+        if (more) store_tile(cur ^ 1u);
+        __syncthreads();
+    }
+
+    // lanes l and l + 32 hold two halves of the same row's ids
+    const float ov = __shfl_xor(best, 32);
+    const uint32_t oi = __shfl_xor(bidx, 32);
+    merge(best, bidx, ov, oi);
+    if (khalf == 0u && row_ok) {
+        a.table[(uint64_t)row * a.ranges + range] = make_key(best, bidx);
+    }
+}
+
+template <int R>
+hipError_t launch_gemm(const GemmArgs& a, uint32_t grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL(gemm_readout_kernel<R>, dim3(grid), dim3(kWaves * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" int xpress_readout_gemm_argmax_to_blk(const uint16_t* base, const uint16_t* x,
+                                                 const uint16_t* w, int64_t* blk, int64_t N,
+                                                 int64_t B, int64_t V, int64_t R,
+                                                 int64_t stride_base_r, hipStream_t stream)
+{
+    if (N < 0 || B < 1 || V < 1 || V > 0x7FFFFFFFll || stride_base_r < V) return XPRESS_EINVAL;
+    if (R != 64 && R != 128 && R != 256) return XPRESS_EINVAL;
+    if (B - 1 > 0 && N > INT64_MAX / (B - 1)) return XPRESS_EINVAL;
+    const int64_t rows = N * (B - 1);
+    if (rows == 0) return XPRESS_OK;
+    if (rows > 0x7FFFFFFFll || N > INT64_MAX / B) return XPRESS_EINVAL;
+    if (!base || !x || !w || !blk) return XPRESS_EINVAL;
+    if (!is_aligned16(base) || !is_aligned16(x) || !is_aligned16(w) || stride_base_r % 8 != 0) {
+        return XPRESS_EINVAL;
+    }
+    if ((rows - 1) > (INT64_MAX / 8 - V) / stride_base_r || V > INT64_MAX / 8 / R) {
+        return XPRESS_EINVAL;
+    }
+    const size_t blk_bytes = (size_t)(N * B) * 8u;
+    if (ranges_overlap(blk, blk_bytes, base, (size_t)((rows - 1) * stride_base_r + V) * 2u) ||
+        ranges_overlap(blk, blk_bytes, x, (size_t)(rows * R) * 2u) ||
+        ranges_overlap(blk, blk_bytes, w, (size_t)(V * R) * 2u)) {
+        return XPRESS_EINVAL;
+    }
+
+    GemmArgs a;
+    a.base = base;
+    a.x = x;
+    a.w = w;
+    a.stride_base = stride_base_r;
+    a.rows = (uint32_t)rows;
+    a.V = (uint32_t)V;
+    a.tiles = (uint32_t)((V + kTileV - 1) / kTileV);
+    const int64_t groups = (rows + 31) / 32;
+    a.row_wgs = (uint32_t)((groups + kWaves - 1) / kWaves);
+    // about two workgroups per CU; ranges a multiple of 8 (one per XCD slot)
+    int64_t ranges = (2 * (int64_t)device_cus()) / a.row_wgs;
+    ranges = ranges / 8 * 8;
+    if (ranges < 8) ranges = 8;
+    const int64_t max_ranges = ((int64_t)a.tiles + 7) / 8 * 8;
+    if (ranges > max_ranges) ranges = max_ranges;
+    if ((int64_t)a.row_wgs * ranges > 0x7FFFFFFFll) return XPRESS_EINVAL;
+    a.ranges = (uint32_t)ranges;
+
+    int rc = workspace_table(stream, rows * ranges, &a.table);
+    if (rc != XPRESS_OK) return rc;
+
+    const uint32_t grid = a.row_wgs * a.ranges;
+    hipError_t e;
+    switch (R) {
+        case 64: e = launch_gemm<64>(a, grid, stream); break;
+        case 128: e = launch_gemm<128>(a, grid, stream); break;
+        default: e = launch_gemm<256>(a, grid, stream); break;
+    }
+    if (e != hipSuccess) return hip_fail(e);
+    e = launch_reduce_table(a.table, blk, a.rows, (uint32_t)(B - 1), a.ranges, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return XPRESS_OK;
+}

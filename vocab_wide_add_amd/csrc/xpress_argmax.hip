@@ -41,140 +41,12 @@
 #include <utility>
 
 #include "xpress_argmax.h"
+#include "device_common.h"
+#include "host_common.h"
 
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-constexpr uint32_t kNoIndex = 0xFFFFFFFFu;  // "no candidate" (loses every tie)
-
-// ---------------------------------------------------------------------------
-// Element step.
-// ---------------------------------------------------------------------------
-
-// The low / high bf16 of a packed pair, widened to fp32 (exact: bf16 is the
-// upper half of binary32).
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// Two element sums at once: a and b each pack two bf16; returns the two sums
-// rounded to bf16 (round-to-nearest-even), packed the same way.  The fp32 sum
-// of two bf16 values rounded to bf16 equals the exact sum rounded once to
-// bf16, since fp32 carries 24 >= 2*8 + 2 significant bits.
-__device__ __forceinline__ uint32_t add_round2(uint32_t a, uint32_t b)
-{
-    f32x2 s;
-    s.x = bf16_lo(a) + bf16_lo(b);
-    s.y = bf16_hi(a) + bf16_hi(b);
-    bf16x2 r = __builtin_convertvector(s, bf16x2);
-    return __builtin_bit_cast(uint32_t, r);
-}
-
-// Scalar form for the unaligned path and the vocabulary tail.
-__device__ __forceinline__ float add_round1(uint16_t a, uint16_t b)
-{
-    uint32_t p = add_round2((uint32_t)a, (uint32_t)b);
-    return bf16_lo(p);
-}
-
-// ---------------------------------------------------------------------------
-// (value, index) order: larger value first, then smaller index.  Float
-// comparison makes -0 equal to +0.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void merge(float& v, uint32_t& i, float ov, uint32_t oi)
-{
-    const bool take = (ov > v) | ((ov == v) & (oi < i));
-    v = take ? ov : v;
-    i = take ? oi : i;
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t x)
-{
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
-}
-
-template <int CTRL>
-__device__ __forceinline__ void merge_dpp(float& v, uint32_t& i)
-{
-    float ov = __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
-    uint32_t oi = dpp_u32<CTRL>(i);
-    merge(v, i, ov, oi);
-}
-
-// Reduce over the 64 lanes of the wave; the result is wave-uniform.
-__device__ __forceinline__ void wave_argmax(float& v, uint32_t& i)
-{
-    merge_dpp<0xB1>(v, i);   // quad_perm [1,0,3,2]: partner lane ^ 1
-    merge_dpp<0x4E>(v, i);   // quad_perm [2,3,0,1]: partner lane ^ 2
-    merge_dpp<0x141>(v, i);  // row_half_mirror: the other quad of each 8
-    merge_dpp<0x140>(v, i);  // row_mirror: the other 8 of each 16
-    // ds_swizzle bit mode, and_mask 0x1F, xor_mask 0x10: partner lane ^ 16
-    float ov = __uint_as_float((uint32_t)__builtin_amdgcn_ds_swizzle(
-        (int)__float_as_uint(v), 0x401F));
-    uint32_t oi = (uint32_t)__builtin_amdgcn_ds_swizzle((int)i, 0x401F);
-    merge(v, i, ov, oi);
-    // lanes 0..31 and 32..63 now each hold their half's result
-    float v0 = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 0));
-    uint32_t i0 = (uint32_t)__builtin_amdgcn_readlane((int)i, 0);
-    float v1 = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 32));
-    uint32_t i1 = (uint32_t)__builtin_amdgcn_readlane((int)i, 32);
-    merge(v0, i0, v1, i1);
-    v = v0;
-    i = i0;
-}
-
-// Workgroup reduction; every thread returns the workgroup's result.
-template <int T>
-__device__ __forceinline__ void block_argmax(float& v, uint32_t& i)
-{
-    constexpr int kWaves = T / 64;
-    wave_argmax(v, i);
-    if constexpr (kWaves > 1) {
-        __shared__ float sv[kWaves];
-        __shared__ uint32_t si[kWaves];
-        const int wave = threadIdx.x / 64;
-        if ((threadIdx.x & 63) == 0) {
-            sv[wave] = v;
-            si[wave] = i;
-        }
-        __syncthreads();
-        float bv = sv[0];
-        uint32_t bi = si[0];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) {
-            merge(bv, bi, sv[w], si[w]);
-        }
-        v = bv;
-        i = bi;
-        __syncthreads();  // sv/si may be reused by the next unit of work
-    }
-}
-
-// Packed order-preserving 48-bit key: (ordered bf16 of the value) << 32 |
-// ~index.  Unsigned order of keys == (value desc, index asc) order of
-// candidates.  -0 is mapped to +0 first so the two compare equal.  A missing
-// candidate is the key 0, below every real key (real keys have ~index >=
-// 2^31).
-__device__ __forceinline__ uint64_t make_key(float v, uint32_t i)
-{
-    if (i == kNoIndex) {
-        return 0;
-    }
-    uint32_t h = __float_as_uint(v) >> 16;  // v is a widened bf16
-    if (h == 0x8000u) {
-        h = 0;
-    }
-    uint32_t ord = (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
-    return ((uint64_t)ord << 32) | (uint64_t)(kNoIndex - i);
-}
-
-__device__ __forceinline__ int64_t key_index(uint64_t key)
-{
-    return (int64_t)(kNoIndex - (uint32_t)(key & 0xFFFFFFFFu));
-}
+using namespace xpress;
 
 // ---------------------------------------------------------------------------
 // Streaming parts.
@@ -534,13 +406,6 @@ __global__ __launch_bounds__(256) void round_table_kernel(const uint16_t* __rest
 // Host side.
 // ---------------------------------------------------------------------------
 
-thread_local int g_last_hip_error = 0;
-
-int hip_fail(hipError_t e)
-{
-    g_last_hip_error = (int)e;
-    return XPRESS_EHIP;
-}
 
 struct Plan {
     int combine;
@@ -550,22 +415,6 @@ struct Plan {
     int launches;
     uint32_t grid;  // kBalanced: total workgroups
 };
-
-// Compute units of the current device, cached per device.
-int device_cus()
-{
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-    if (dev < 64 && cached[dev] > 0) return cached[dev];
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0) {
-        n = 256;
-    }
-    if (dev < 64) cached[dev] = n;
-    return n;
-}
 
 std::mutex g_plan_mu;
 int g_override_combine = XPRESS_COMBINE_AUTO;
@@ -592,7 +441,6 @@ constexpr int64_t kBalancedPerCu = 2;
 // 2.8 / 3.1 / 3.1 / 3.3 us.
 constexpr int64_t kTopcWaveMaxC = 256;
 
-bool is_aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Workgroup size of the default plan.  Measured on MI355X with one
 // workgroup per row (interleaved medians): at 480 rows x 152064, 256 threads
@@ -720,7 +568,7 @@ int ensure_workspace(hipStream_t stream, int64_t rows, int64_t table, Workspace*
         void* p = nullptr;
         e = hipMalloc(&p, (size_t)cap * 8u);
         if (e != hipSuccess) {
-            g_last_hip_error = (int)e;
+            note_hip_error(e);
             return XPRESS_ENOMEM;
         }
         e = hipMemset(p, 0, (size_t)cap * 8u);
@@ -742,7 +590,7 @@ int ensure_workspace(hipStream_t stream, int64_t rows, int64_t table, Workspace*
         void* p = nullptr;
         e = hipMalloc(&p, (size_t)cap * 8u);
         if (e != hipSuccess) {
-            g_last_hip_error = (int)e;
+            note_hip_error(e);
             return XPRESS_ENOMEM;
         }
         if (w.table) (void)hipFree(w.table);
@@ -808,12 +656,6 @@ hipError_t launch_plan(const RowArgs& a, const Plan& p, hipStream_t stream)
     }
 }
 
-bool ranges_overlap(const void* p0, size_t n0, const void* p1, size_t n1)
-{
-    const uintptr_t a0 = reinterpret_cast<uintptr_t>(p0), a1 = a0 + n0;
-    const uintptr_t b0 = reinterpret_cast<uintptr_t>(p1), b1 = b0 + n1;
-    return a0 < b1 && b0 < a1;
-}
 
 int validate(const uint16_t* base, const uint16_t* bias, const int64_t* blk, int64_t N,
              int64_t B, int64_t V, int64_t sb, int64_t sbi, const int64_t* cand,
@@ -880,15 +722,75 @@ int run_readout(const uint16_t* base, const uint16_t* bias, const int64_t* cand,
     hipError_t e = launch_plan(a, p, stream);
     if (e != hipSuccess) return hip_fail(e);
     if (p.combine == kTwoPass) {
-        const uint32_t grid = (uint32_t)((rows + 255) / 256 < 65536 ? (rows + 255) / 256 : 65536);
-        hipLaunchKernelGGL(reduce_keys_kernel, dim3(grid), dim3(256), 0, stream, a);
-        e = hipGetLastError();
+        e = launch_reduce_table(a.keys, blk, a.rows, a.bm1, a.splits, stream);
         if (e != hipSuccess) return hip_fail(e);
     }
     return XPRESS_OK;
 }
 
 }  // namespace
+
+namespace xpress {
+
+XPRESS_INTERNAL thread_local int g_last_hip_error = 0;
+
+void note_hip_error(hipError_t e) { g_last_hip_error = (int)e; }
+
+int hip_fail(hipError_t e)
+{
+    g_last_hip_error = (int)e;
+    return XPRESS_EHIP;
+}
+
+int device_cus()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0) {
+        n = 256;
+    }
+    if (dev < 64) cached[dev] = n;
+    return n;
+}
+
+bool is_aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool ranges_overlap(const void* p0, size_t n0, const void* p1, size_t n1)
+{
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(p0), a1 = a0 + n0;
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(p1), b1 = b0 + n1;
+    return a0 < b1 && b0 < a1;
+}
+
+int workspace_table(hipStream_t stream, int64_t entries, uint64_t** table)
+{
+    Workspace* w = nullptr;
+    const int rc = ensure_workspace(stream, 0, entries, &w);
+    if (rc != XPRESS_OK) return rc;
+    *table = w->table;
+    return XPRESS_OK;
+}
+
+hipError_t launch_reduce_table(uint64_t* table, int64_t* blk, uint32_t rows, uint32_t bm1,
+                               uint32_t splits, hipStream_t stream)
+{
+    RowArgs a = {};
+    a.blk = blk;
+    a.rows = rows;
+    a.bm1 = bm1;
+    a.splits = splits;
+    a.keys = table;
+    a.cand = nullptr;
+    const uint32_t grid = (rows + 255u) / 256u < 65536u ? (rows + 255u) / 256u : 65536u;
+    hipLaunchKernelGGL(reduce_keys_kernel, dim3(grid), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace xpress
 
 extern "C" {
 
@@ -1019,7 +921,7 @@ int xpress_bf16_add_round_table(const uint16_t* a_vals, int64_t n_a, uint16_t* o
     return XPRESS_OK;
 }
 
-int xpress_last_hip_error(void) { return g_last_hip_error; }
+int xpress_last_hip_error(void) { return xpress::g_last_hip_error; }
 
 const char* xpress_error_string(int status)
 {

@@ -59,6 +59,9 @@ def load():
         lib.xpress_add_argmax_to_blk.restype = i32
         lib.xpress_topc_argmax_to_blk.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
         lib.xpress_topc_argmax_to_blk.restype = i32
+        lib.xpress_readout_gemm_argmax_to_blk.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64,
+                                                          i64, vp]
+        lib.xpress_readout_gemm_argmax_to_blk.restype = i32
         lib.xpress_reserve.argtypes = [i64, i64, i64, vp]
         lib.xpress_reserve.restype = i32
         lib.xpress_release.argtypes = []
@@ -130,6 +133,17 @@ def xpress_topc_argmax_to_blk(base_c, bias_c, cand, blk, N: int, B: int, C: int,
     _check(lib.xpress_topc_argmax_to_blk(_ptr(base_c), _ptr(bias_c), _ptr(cand), _ptr(blk),
                                          int(N), int(B), int(C), _stream(stream)),
            "xpress_topc_argmax_to_blk")
+
+
+def xpress_readout_gemm_argmax_to_blk(base, x, w, blk, N: int, B: int, V: int, R: int,
+                                      stride_base_r: int, stream=None) -> None:
+    """blk[n, 1+b] = argmax_v bf16(base[r, v] + bf16(x[r] . w[v])), r = n*(B-1) + b;
+    x is [rows, R], w is [V, R], all bf16 on the GPU."""
+    lib = load()
+    _check(lib.xpress_readout_gemm_argmax_to_blk(_ptr(base), _ptr(x), _ptr(w), _ptr(blk),
+                                                 int(N), int(B), int(V), int(R),
+                                                 int(stride_base_r), _stream(stream)),
+           "xpress_readout_gemm_argmax_to_blk")
 
 
 def xpress_reserve(N: int, B: int, V: int, stream=None) -> None:
