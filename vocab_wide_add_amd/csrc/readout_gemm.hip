@@ -38,6 +38,8 @@
 
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "xpress_argmax.h"
 #include "device_common.h"
 #include "host_common.h"
@@ -51,7 +53,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTileV = 64;   // vocabulary ids per tile: two 32-id MFMA slices
-constexpr int kWaves = 4;    // waves (32-row groups) per workgroup
+constexpr int kWaves = 8;    // waves (32-row groups) per workgroup
 
 struct GemmArgs {
     const uint16_t* base;
@@ -138,8 +140,14 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
         }
     };
 
+    // Running first maximum of this lane's ids.  It starts at the lane's
+    // first id (below V whenever the range has a tile) with value -inf and
+    // only a strictly larger value replaces it, so a lane whose values are
+    // all -inf still reports its first id.  Lanes of rows past the last row
+    // compute on zeros and never publish.
     float best = -__builtin_inff();
-    uint32_t bidx = kNoIndex;
+    const uint32_t first_id = t0 * kTileV + 4u * khalf;
+    uint32_t bidx = (t0 < t1 && first_id < a.V) ? first_id : kNoIndex;
 
     if (t0 < t1) {
         load_tile(t0);
@@ -147,64 +155,81 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
     }
     __syncthreads();
 
-    for (uint32_t t = t0; t < t1; ++t) {
-        const uint32_t cur = (t - t0) & 1u;
-        const bool more = t + 1u < t1;
-        if (more) load_tile(t + 1u);
+    // invalid rows read row 0 (always in bounds) and never update
+    const uint16_t* brow = a.base + (int64_t)(row_ok ? row : 0u) * a.stride_base;
 
-        // base for this tile: per slice g and run q, 4 consecutive ids
-        u32x2 bv[2][4];
+    // base for one tile: per slice g and run q, the 4 consecutive ids this
+    // lane's accumulators hold.  FULL tiles use plain 8-byte loads; the last
+    // tile of a ragged vocabulary reads each id at min(id, V - 1) -- in
+    // bounds, masked out past V.
+    auto load_base = [&](uint32_t t, u32x2 (&bv)[2][4], auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        const uint32_t tv = t * kTileV;
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const uint32_t v = t * kTileV + 32u * g + 8u * q + 4u * khalf;
-                u32x2 val = {0u, 0u};
-                if (row_ok) {
-                    const uint16_t* p = a.base + (int64_t)row * a.stride_base + v;
-                    if (v + 3u < a.V) {
-                        val = *reinterpret_cast<const u32x2*>(p);
-                    } else {
-                        uint16_t e[4] = {0, 0, 0, 0};
-                        for (uint32_t j = 0; j < 4u; ++j) {
-                            if (v + j < a.V) e[j] = p[j];
-                        }
-                        val.x = (uint32_t)e[0] | ((uint32_t)e[1] << 16);
-                        val.y = (uint32_t)e[2] | ((uint32_t)e[3] << 16);
+                const uint32_t v = tv + 32u * g + 8u * q + 4u * khalf;
+                if constexpr (FULL) {
+                    bv[g][q] = *reinterpret_cast<const u32x2*>(brow + v);
+                } else {
+                    uint32_t e[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t vj = (v + j < a.V) ? v + j : a.V - 1u;
+                        e[j] = brow[vj];
                     }
+                    bv[g][q].x = e[0] | (e[1] << 16);
+                    bv[g][q].y = e[2] | (e[3] << 16);
                 }
-                bv[g][q] = val;
             }
         }
+    };
 
-        f32x16 acc[2];
+    // One tile: the next tile's base (when it is a full one) and w loads go
+    // out first and stay in flight; the MFMAs run on the current LDS tile and
+    // the epilogue on base loaded one tile earlier; then the next w tile goes
+    // into the other LDS buffer.
+    auto tile = [&](uint32_t t, u32x2 (&bv)[2][4], u32x2 (&bv_next)[2][4], uint32_t full_end,
+                    auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        const uint32_t cur = (t - t0) & 1u;
+        const bool more = t + 1u < t1;
+        const uint32_t tv = t * kTileV;
+        if (t + 1u < full_end) load_base(t + 1u, bv_next, std::true_type{});
+        if (more) load_tile(t + 1u);
+
+        // two independent accumulator chains (the tile's two 32-id slices)
+        f32x16 acc0 = f32x16{};
+        f32x16 acc1 = f32x16{};
+        const unsigned char* arow0 = &lds[cur][(lane & 31u) * ROWB + 16u * khalf];
+        const unsigned char* arow1 = arow0 + 32 * ROWB;
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            acc[g] = f32x16{};
-            const unsigned char* arow = &lds[cur][(32u * g + (lane & 31u)) * ROWB + 16u * khalf];
-#pragma unroll
-            for (int c = 0; c < KC; ++c) {
-                const bf16x8 av =
-                    __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(arow + 32 * c));
-                acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bx[c], acc[g], 0, 0, 0);
-            }
+        for (int c = 0; c < KC; ++c) {
+            const bf16x8 a0 =
+                __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(arow0 + 32 * c));
+            const bf16x8 a1 =
+                __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(arow1 + 32 * c));
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bx[c], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bx[c], acc1, 0, 0, 0);
         }
 
         // epilogue: bias rounded to bf16, added to base, rounded; ascending ids
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
+            const f32x16& acc = g ? acc1 : acc0;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const uint32_t v = t * kTileV + 32u * g + 8u * q + 4u * khalf;
+                const uint32_t v = tv + 32u * g + 8u * q + 4u * khalf;
                 const uint32_t s01 = add_round2(bv[g][q].x,
-                                                round_pack2(acc[g][4 * q], acc[g][4 * q + 1]));
+                                                round_pack2(acc[4 * q], acc[4 * q + 1]));
                 const uint32_t s23 = add_round2(bv[g][q].y,
-                                                round_pack2(acc[g][4 * q + 2], acc[g][4 * q + 3]));
+                                                round_pack2(acc[4 * q + 2], acc[4 * q + 3]));
                 const float sv[4] = {bf16_lo(s01), bf16_hi(s01), bf16_lo(s23), bf16_hi(s23)};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const bool ok = row_ok && (v + j < a.V);
-                    const bool take = ok && ((sv[j] > best) | (bidx == kNoIndex));
+                    // ids past V exist only in a ragged last tile
+                    const bool take = FULL ? (sv[j] > best) : ((v + j < a.V) && (sv[j] > best));
                     best = take ? sv[j] : best;
                     bidx = take ? v + j : bidx;
                 }
@@ -213,6 +238,27 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
 
         if (more) store_tile(cur ^ 1u);
         __syncthreads();
+    };
+
+    if (t0 < t1) {
+        // tiles below full_end are full; a ragged vocabulary's last tile is not
+        const uint32_t full_end = (t1 * kTileV <= a.V) ? t1 : t1 - 1u;
+        u32x2 bvA[2][4], bvB[2][4];
+        if (t0 < full_end) load_base(t0, bvA, std::true_type{});
+        // two tiles per trip: the base buffers alternate without copies
+        uint32_t t = t0;
+        for (; t + 1u < full_end; t += 2u) {
+            tile(t, bvA, bvB, full_end, std::true_type{});
+            tile(t + 1u, bvB, bvA, full_end, std::true_type{});
+        }
+        if (t < full_end) {
+            tile(t, bvA, bvB, full_end, std::true_type{});
+            ++t;
+        }
+        if (t < t1) {
+            load_base(t, bvA, std::false_type{});
+            tile(t, bvA, bvB, full_end, std::false_type{});
+        }
     }
 
     // lanes l and l + 32 hold two halves of the same row's ids
@@ -268,8 +314,9 @@ extern "C" int xpress_readout_gemm_argmax_to_blk(const uint16_t* base, const uin
     a.tiles = (uint32_t)((V + kTileV - 1) / kTileV);
     const int64_t groups = (rows + 31) / 32;
     a.row_wgs = (uint32_t)((groups + kWaves - 1) / kWaves);
-    // about two workgroups per CU; ranges a multiple of 8 (one per XCD slot)
-    int64_t ranges = (2 * (int64_t)device_cus()) / a.row_wgs;
+    // about one workgroup per CU (a workgroup fills its CU's LDS and two
+    // waves per SIMD); ranges a multiple of 8 (one per XCD slot)
+    int64_t ranges = (int64_t)device_cus() / a.row_wgs;
     ranges = ranges / 8 * 8;
     if (ranges < 8) ranges = 8;
     const int64_t max_ranges = ((int64_t)a.tiles + 7) / 8 * 8;
