@@ -75,6 +75,10 @@ def _load():
         lib.oracle_gemm_argmax_rows.argtypes = [
             _U16P, _U16P, _U16P, _I64P] + [ctypes.c_int64] * 5
         lib.oracle_gemm_argmax_rows.restype = ctypes.c_int
+        _DP = ctypes.POINTER(ctypes.c_double)
+        lib.oracle_latent_pass.argtypes = (
+            [_I64P, _I64P] + [_U16P] * 7 + [_U16P] + [ctypes.c_int64] * 5 + [_DP] * 6)
+        lib.oracle_latent_pass.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -263,3 +267,59 @@ def gemm_argmax_rows(base, x, w, rows, V: int, R: int, stride_base_r: int,
     for t in ts:
         t.join()
     return out
+
+
+def latent_pass(blk, am1, xh, w1, wlat, mixl, wg, wu, wd, N: int, B: int, R: int,
+                H: int, V: int, intermediates: bool = False, threads: int = 1):
+    """Latent stage of one pass on host arrays (see ``oracle_latent_pass``).
+
+    blk [N, B] and am1 [N] are int64; xh [N, B, R], w1 [V, R], wlat [R, R],
+    mixl [B, B, R], wg / wu [H, R] and wd [R, H] are uint16 bf16 patterns.
+    Returns out [N, B-1, R] as uint16 bf16 patterns, and with
+    ``intermediates`` also a dict of the binary64 values before rounding:
+    x / u [N, B, R], g / v / f [N, B-1, H], o [N, B-1, R].  Blocks are
+    independent, so they are spread over host threads."""
+    blk = np.ascontiguousarray(blk, dtype=np.int64).reshape(N, B)
+    am1 = np.ascontiguousarray(am1, dtype=np.int64).reshape(N)
+    xh = _u16(xh).reshape(N, B, R)
+    w1 = _u16(w1).reshape(V, R)
+    wlat = _u16(wlat).reshape(R, R)
+    mixl = _u16(mixl).reshape(B, B, R)
+    wg = _u16(wg).reshape(H, R)
+    wu = _u16(wu).reshape(H, R)
+    wd = _u16(wd).reshape(R, H)
+    out = np.zeros((N, B - 1, R), dtype=np.uint16)
+    inter = None
+    if intermediates:
+        inter = {"x": np.zeros((N, B, R)), "u": np.zeros((N, B, R)),
+                 "g": np.zeros((N, B - 1, H)), "v": np.zeros((N, B - 1, H)),
+                 "f": np.zeros((N, B - 1, H)), "o": np.zeros((N, B - 1, R))}
+    lib = _load()
+    dp = ctypes.POINTER(ctypes.c_double)
+    errors = []
+
+    def dptr(name, n0):
+        if inter is None:
+            return ctypes.cast(None, dp)
+        return inter[name][n0:].ctypes.data_as(dp)
+
+    def work(n0, n1):
+        rc = lib.oracle_latent_pass(
+            blk[n0:].ctypes.data_as(_I64P), am1[n0:].ctypes.data_as(_I64P),
+            _p16(xh[n0:]), _p16(w1), _p16(wlat), _p16(mixl), _p16(wg), _p16(wu),
+            _p16(wd), _p16(out[n0:]), n1 - n0, B, R, H, V,
+            dptr("x", n0), dptr("u", n0), dptr("g", n0), dptr("v", n0),
+            dptr("f", n0), dptr("o", n0))
+        if rc != 0:
+            errors.append(rc)
+
+    threads = max(1, min(int(threads), N if N else 1))
+    bounds = [(N * t // threads, N * (t + 1) // threads) for t in range(threads)]
+    ts = [threading.Thread(target=work, args=b) for b in bounds if b[1] > b[0]]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    if errors:
+        raise ValueError("oracle rejected the latent inputs (code %d)" % errors[0])
+    return (out, inter) if intermediates else out

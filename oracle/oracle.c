@@ -36,6 +36,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 /* ---------------------------------------------------------------------------
  * bf16 decoding, from the field definition.
@@ -293,4 +294,148 @@ int oracle_gemm_argmax_rows(const uint16_t* base, const uint16_t* x, const uint1
         idx_out[r - r0] = oracle_gemm_argmax_row(base + r * stride_base_r, x + r * R, w, V, R);
     }
     return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Latent stage of one Jacobi pass (XPress kernels page, module description and
+ * "_xpress_latent_kernel", both revisions): for every block n and slot b < B,
+ * with R latent channels and an MLP of H hidden units,
+ *
+ *   prev[b]  = am1[n] for b = 0, blk[n, b-1] otherwise   (previous slot's token)
+ *   x[b, r]  = xh[n, b, r] + sum_k w1[prev[b], k] * wlat[r, k]
+ *   u[b, r]  = sum_j mixl[b, j, r] * x[j, r]               (folded causal mixer)
+ *   g[b, h]  = sum_r bf16(u[b, r]) * wg[h, r]
+ *   v[b, h]  = sum_r bf16(u[b, r]) * wu[h, r]
+ *   f[b, h]  = g * sigmoid(g) * v                          (SwiGLU)
+ *   o[b, r]  = u[b, r] + sum_h bf16(f[b, h]) * wd[r, h]    (MLP with residual)
+ *   out[n, b-1, r] = bf16(o[b, r]),  b = 1 .. B-1
+ *
+ * All tensors are bf16 bit patterns except blk / am1 (int64).  Weight layouts
+ * are out-major (one row per output unit): wlat [R, R], wg / wu [H, R],
+ * wd [R, H]; mixl is [B, B, R] (zero above the diagonal for a causal mixer, but
+ * every j < B is summed, as the page's mixer loop does); xh is [N, B, R]; w1 is
+ * [V, R]; out is [N, B-1, R].  Slot 0 is the anchor: its x feeds the mixer of
+ * the later slots but no latent is written for it.
+ *
+ * Reading: the page's kernel keeps x, u, g, v and the residual sum in fp32 and
+ * rounds to bf16 at exactly three places: u before the MLP, the SwiGLU product
+ * before the down projection, and the output.  The plain definition of each
+ * fp32 quantity is its exact real value; here it is formed in binary64 (every
+ * product of two bf16 values is exact there) and the sigmoid is the C
+ * library's exp.
+ *
+ * Optional outputs (NULL to skip), binary64 before any rounding:
+ *   xs [N, B, R], us [N, B, R], gs / vs / fs [N, B-1, H], os [N, B-1, R].
+ * Returns 0, -1 on invalid sizes or a token id outside [0, V), -2 when out of
+ * host memory.
+ * ------------------------------------------------------------------------- */
+int oracle_latent_pass(const int64_t* blk, const int64_t* am1, const uint16_t* xh,
+                       const uint16_t* w1, const uint16_t* wlat, const uint16_t* mixl,
+                       const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
+                       uint16_t* out, int64_t N, int64_t B, int64_t R, int64_t H,
+                       int64_t V, double* xs, double* us, double* gs, double* vs,
+                       double* fs, double* os)
+{
+    if (N < 0 || B < 2 || R < 1 || H < 1 || V < 1) {
+        return -1;
+    }
+    /* the weights decoded to binary64 once (a change of storage, not of the
+       arithmetic below) */
+    double* dlat = (double*)malloc(sizeof(double) * (size_t)(R * R));
+    double* dmix = (double*)malloc(sizeof(double) * (size_t)(B * B * R));
+    double* dg = (double*)malloc(sizeof(double) * (size_t)(H * R));
+    double* du = (double*)malloc(sizeof(double) * (size_t)(H * R));
+    double* dd = (double*)malloc(sizeof(double) * (size_t)(R * H));
+    double* emb = (double*)malloc(sizeof(double) * (size_t)R);
+    double* x = (double*)malloc(sizeof(double) * (size_t)(B * R));
+    double* u = (double*)malloc(sizeof(double) * (size_t)(B * R));
+    double* ub = (double*)malloc(sizeof(double) * (size_t)R);
+    double* m = (double*)malloc(sizeof(double) * (size_t)H);
+    int rc = 0;
+    if (!dlat || !dmix || !dg || !du || !dd || !emb || !x || !u || !ub || !m) {
+        rc = -2;
+        goto done;
+    }
+    for (int64_t i = 0; i < R * R; ++i) dlat[i] = oracle_bf16_to_double(wlat[i]);
+    for (int64_t i = 0; i < B * B * R; ++i) dmix[i] = oracle_bf16_to_double(mixl[i]);
+    for (int64_t i = 0; i < H * R; ++i) {
+        dg[i] = oracle_bf16_to_double(wg[i]);
+        du[i] = oracle_bf16_to_double(wu[i]);
+        dd[i] = oracle_bf16_to_double(wd[i]);
+    }
+    for (int64_t n = 0; n < N; ++n) {
+        /* embedding of the previous slot's token, projected, plus the cache */
+        for (int64_t b = 0; b < B; ++b) {
+            int64_t tok = (b == 0) ? am1[n] : blk[n * B + b - 1];
+            if (tok < 0 || tok >= V) {
+                rc = -1;
+                goto done;
+            }
+            for (int64_t k = 0; k < R; ++k) {
+                emb[k] = oracle_bf16_to_double(w1[tok * R + k]);
+            }
+            for (int64_t r = 0; r < R; ++r) {
+                double acc = oracle_bf16_to_double(xh[(n * B + b) * R + r]);
+                for (int64_t k = 0; k < R; ++k) {
+                    acc += emb[k] * dlat[r * R + k];
+                }
+                x[b * R + r] = acc;
+            }
+        }
+        /* folded causal mixer, per channel */
+        for (int64_t b = 0; b < B; ++b) {
+            for (int64_t r = 0; r < R; ++r) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < B; ++j) {
+                    acc += dmix[(b * B + j) * R + r] * x[j * R + r];
+                }
+                u[b * R + r] = acc;
+            }
+        }
+        if (xs != NULL || us != NULL) {
+            for (int64_t i = 0; i < B * R; ++i) {
+                if (xs != NULL) xs[n * B * R + i] = x[i];
+                if (us != NULL) us[n * B * R + i] = u[i];
+            }
+        }
+        /* SwiGLU MLP with residual, for the slots that are read out */
+        for (int64_t b = 1; b < B; ++b) {
+            int64_t row = n * (B - 1) + b - 1;
+            for (int64_t r = 0; r < R; ++r) {
+                ub[r] = oracle_bf16_to_double(oracle_bf16_from_double(u[b * R + r]));
+            }
+            for (int64_t h = 0; h < H; ++h) {
+                double g = 0.0, v = 0.0;
+                for (int64_t r = 0; r < R; ++r) {
+                    g += ub[r] * dg[h * R + r];
+                    v += ub[r] * du[h * R + r];
+                }
+                double f = g / (1.0 + exp(-g)) * v;
+                m[h] = oracle_bf16_to_double(oracle_bf16_from_double(f));
+                if (gs != NULL) gs[row * H + h] = g;
+                if (vs != NULL) vs[row * H + h] = v;
+                if (fs != NULL) fs[row * H + h] = f;
+            }
+            for (int64_t r = 0; r < R; ++r) {
+                double acc = u[b * R + r];
+                for (int64_t h = 0; h < H; ++h) {
+                    acc += m[h] * dd[r * H + h];
+                }
+                if (os != NULL) os[row * R + r] = acc;
+                out[row * R + r] = oracle_bf16_from_double(acc);
+            }
+        }
+    }
+done:
+    free(dlat);
+    free(dmix);
+    free(dg);
+    free(du);
+    free(dd);
+    free(emb);
+    free(x);
+    free(u);
+    free(ub);
+    free(m);
+    return rc;
 }

@@ -14,6 +14,7 @@ import pytest
 
 import exact_bf16
 from test_oracle import ARGMAX_ROWS, GEMM_ROWS, ROUNDING, TOPC_ROWS
+from test_oracle_latent import latent_pins_pass
 from vocab_wide_add_amd import workloads
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -49,7 +50,72 @@ MUTATIONS = {
                            "oracle_gemm_argmax_row(base + r * stride_base_r, x, w, V, R)"),
     "gemm_bias_unrounded": ("return oracle_bf16_from_double(acc);",
                             "return oracle_bf16_from_double(acc) | 1;"),
+    # latent stage
+    "latent_prev_is_same_slot": ("int64_t tok = (b == 0) ? am1[n] : blk[n * B + b - 1];",
+                                 "int64_t tok = (b == 0) ? am1[n] : blk[n * B + b];"),
+    "latent_anchor_not_am1": ("int64_t tok = (b == 0) ? am1[n] : blk[n * B + b - 1];",
+                              "int64_t tok = (b == 0) ? blk[n * B] : blk[n * B + b - 1];"),
+    "latent_cache_dropped": ("double acc = oracle_bf16_to_double(xh[(n * B + b) * R + r]);",
+                             "double acc = 0.0;"),
+    "latent_wlat_transposed": ("acc += emb[k] * dlat[r * R + k];",
+                               "acc += emb[k] * dlat[k * R + r];"),
+    "latent_mixer_transposed": ("acc += dmix[(b * B + j) * R + r] * x[j * R + r];",
+                                "acc += dmix[(j * B + b) * R + r] * x[j * R + r];"),
+    "latent_mixer_causal_only": ("for (int64_t j = 0; j < B; ++j) {\n                    acc += dmix",
+                                 "for (int64_t j = 0; j <= b; ++j) {\n                    acc += dmix"),
+    "latent_ub_unrounded": ("ub[r] = oracle_bf16_to_double(oracle_bf16_from_double(u[b * R + r]));",
+                            "ub[r] = u[b * R + r];"),
+    "latent_gate_reads_up": ("g += ub[r] * dg[h * R + r];", "g += ub[r] * du[h * R + r];"),
+    "latent_silu_sign": ("double f = g / (1.0 + exp(-g)) * v;",
+                         "double f = g / (1.0 + exp(g)) * v;"),
+    "latent_m_unrounded": ("m[h] = oracle_bf16_to_double(oracle_bf16_from_double(f));",
+                           "m[h] = f;"),
+    "latent_residual_dropped": ("double acc = u[b * R + r];\n                for (int64_t h",
+                                "double acc = 0.0;\n                for (int64_t h"),
+    "latent_residual_rounded": ("double acc = u[b * R + r];\n                for (int64_t h",
+                                "double acc = ub[r];\n                for (int64_t h"),
+    "latent_down_transposed": ("acc += m[h] * dd[r * H + h];", "acc += m[h] * dd[h * R + r];"),
+    "latent_block_stride_B": ("int64_t row = n * (B - 1) + b - 1;", "int64_t row = n * B + b - 1;"),
 }
+
+
+def _bind(lib):
+    lib.oracle_bf16_sum.argtypes = [ctypes.c_uint16, ctypes.c_uint16]
+    lib.oracle_bf16_sum.restype = ctypes.c_uint16
+    lib.oracle_add_argmax_row.argtypes = [U16P, U16P, ctypes.c_int64]
+    lib.oracle_add_argmax_row.restype = ctypes.c_int64
+    lib.oracle_add_argmax_to_blk.argtypes = [U16P, U16P, I64P] + [ctypes.c_int64] * 5
+    lib.oracle_add_argmax_to_blk.restype = ctypes.c_int
+    lib.oracle_topc_argmax_to_blk.argtypes = [U16P, U16P, I64P, I64P] + [ctypes.c_int64] * 3
+    lib.oracle_topc_argmax_to_blk.restype = ctypes.c_int
+    lib.oracle_gemm_argmax_rows.argtypes = [U16P, U16P, U16P, I64P] + [ctypes.c_int64] * 5
+    lib.oracle_gemm_argmax_rows.restype = ctypes.c_int
+    DP = ctypes.POINTER(ctypes.c_double)
+    lib.oracle_latent_pass.argtypes = [I64P, I64P] + [U16P] * 8 + [ctypes.c_int64] * 5 + [DP] * 6
+    lib.oracle_latent_pass.restype = ctypes.c_int
+    return lib
+
+
+def _latent_caller(lib):
+    """A latent-pass callable over a (possibly mutated) library.  The output
+    buffer is padded to N*B*R so that a mutant writing past N*(B-1)*R stays
+    inside memory it owns; only the first N*(B-1)*R elements are compared."""
+    DP = ctypes.POINTER(ctypes.c_double)
+
+    def call(blk, am1, xh, w1, wlat, mixl, wg, wu, wd, N, B, R, H, V):
+        arrs = [np.ascontiguousarray(a) for a in (xh, w1, wlat, mixl, wg, wu, wd)]
+        blk = np.ascontiguousarray(blk, dtype=np.int64)
+        am1 = np.ascontiguousarray(am1, dtype=np.int64)
+        out = np.zeros(N * B * R + 1, dtype=np.uint16)
+        null = ctypes.cast(None, DP)
+        rc = lib.oracle_latent_pass(blk.ctypes.data_as(I64P), am1.ctypes.data_as(I64P),
+                                    *[a.ctypes.data_as(U16P) for a in arrs],
+                                    out.ctypes.data_as(U16P), N, B, R, H, V,
+                                    null, null, null, null, null, null)
+        if rc != 0:
+            raise ValueError("rejected")
+        return out[:N * (B - 1) * R].reshape(N, B - 1, R)
+    return call
 
 
 def _build_mutant(tmp_path, name):
@@ -61,18 +127,7 @@ def _build_mutant(tmp_path, name):
     open(path_c, "w").write(src.replace(old, new))
     subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
                     "-w", "-o", path_so, path_c, "-lm"], check=True)
-    lib = ctypes.CDLL(path_so)
-    lib.oracle_bf16_sum.argtypes = [ctypes.c_uint16, ctypes.c_uint16]
-    lib.oracle_bf16_sum.restype = ctypes.c_uint16
-    lib.oracle_add_argmax_row.argtypes = [U16P, U16P, ctypes.c_int64]
-    lib.oracle_add_argmax_row.restype = ctypes.c_int64
-    lib.oracle_add_argmax_to_blk.argtypes = [U16P, U16P, I64P] + [ctypes.c_int64] * 5
-    lib.oracle_add_argmax_to_blk.restype = ctypes.c_int
-    lib.oracle_topc_argmax_to_blk.argtypes = [U16P, U16P, I64P, I64P] + [ctypes.c_int64] * 3
-    lib.oracle_topc_argmax_to_blk.restype = ctypes.c_int
-    lib.oracle_gemm_argmax_rows.argtypes = [U16P, U16P, U16P, I64P] + [ctypes.c_int64] * 5
-    lib.oracle_gemm_argmax_rows.restype = ctypes.c_int
-    return lib
+    return _bind(ctypes.CDLL(path_so))
 
 
 def _pins_pass(lib) -> bool:
@@ -138,6 +193,11 @@ def _pins_pass(lib) -> bool:
                                 w.ctypes.data_as(U16P), out.ctypes.data_as(I64P), 0, 2, 2, 2, 2)
     if list(out) != [0, 1]:
         return False
+    try:
+        if not latent_pins_pass(_latent_caller(lib)):
+            return False
+    except ValueError:
+        return False
     return True
 
 
@@ -149,18 +209,7 @@ def test_unmutated_oracle_passes_the_pins(tmp_path):
     open(path_c, "w").write(src)
     subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
                     "-o", path_so, path_c, "-lm"], check=True)
-    lib = ctypes.CDLL(path_so)
-    lib.oracle_bf16_sum.argtypes = [ctypes.c_uint16, ctypes.c_uint16]
-    lib.oracle_bf16_sum.restype = ctypes.c_uint16
-    lib.oracle_add_argmax_row.argtypes = [U16P, U16P, ctypes.c_int64]
-    lib.oracle_add_argmax_row.restype = ctypes.c_int64
-    lib.oracle_add_argmax_to_blk.argtypes = [U16P, U16P, I64P] + [ctypes.c_int64] * 5
-    lib.oracle_add_argmax_to_blk.restype = ctypes.c_int
-    lib.oracle_topc_argmax_to_blk.argtypes = [U16P, U16P, I64P, I64P] + [ctypes.c_int64] * 3
-    lib.oracle_topc_argmax_to_blk.restype = ctypes.c_int
-    lib.oracle_gemm_argmax_rows.argtypes = [U16P, U16P, U16P, I64P] + [ctypes.c_int64] * 5
-    lib.oracle_gemm_argmax_rows.restype = ctypes.c_int
-    assert _pins_pass(lib)
+    assert _pins_pass(_bind(ctypes.CDLL(path_so)))
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))

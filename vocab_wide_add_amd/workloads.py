@@ -320,3 +320,132 @@ def generate_gemm(w: GemmWorkload, rows_limit: Optional[int] = None):
     blk = np.full((w.N, w.B), -1, dtype=np.int64)
     blk[:, 0] = gi.integers(0, w.V, size=w.N)
     return f32_to_bf16_bits(base), f32_to_bf16_bits(x), f32_to_bf16_bits(wt), blk
+
+
+# ---------------------------------------------------------------------------
+# Latent stage of one pass: per block the previous slot's token ids, the
+# hidden cache, and the synthetic weights of the embedding, the projection
+# W_lat, the folded causal mixer and the SwiGLU MLP.
+# ---------------------------------------------------------------------------
+
+
+@dataclasses.dataclass(frozen=True)
+class LatentWorkload:
+    name: str
+    N: int
+    B: int
+    R: int
+    H: int
+    V: int
+    seed: int
+    # "causal": mixer = I + L on and below the diagonal (the folded form
+    #           L * tril + I), zero above;
+    # "full":   mixer = I + L everywhere (checks that every slot is summed);
+    # "exact":  dyadic values and wg = wu = 0, so every fp32 sum is exact,
+    #           the MLP adds exactly 0 and the output is bf16(u) with many
+    #           exact ties.
+    kind: str = "causal"
+
+    @property
+    def rows(self) -> int:
+        """Latent rows written: slots 1..B-1 of every block."""
+        return self.N * (self.B - 1)
+
+    @property
+    def weight_bytes(self) -> int:
+        """W_lat, the mixer and the three MLP matrices, bf16."""
+        return 2 * (self.R * self.R + self.B * self.B * self.R + 3 * self.H * self.R)
+
+    @property
+    def bytes_moved(self) -> int:
+        """Algorithmic HBM bytes of one pass: the weights once, per block the
+        ids (8 B per slot plus am1), the hidden cache and the gathered
+        embedding rows (2 B per channel per slot), and the bf16 output."""
+        per_block = 8 * (self.B + 1) + 2 * self.B * self.R * 2 + 2 * (self.B - 1) * self.R
+        return self.weight_bytes + self.N * per_block
+
+    @property
+    def flops(self) -> int:
+        """Multiply-adds times two: the projection for every slot, the mixer,
+        and the MLP (gate, up, down) for the slots that are read out."""
+        proj = self.N * self.B * self.R * self.R
+        mix = self.N * self.B * self.B * self.R
+        mlp = self.rows * 3 * self.H * self.R
+        return 2 * (proj + mix + mlp)
+
+
+LATENT_WORKLOADS = {
+    w.name: w
+    for w in [
+        LatentWorkload("latent_tiny_n2_b4_r64_h128_v1000", 2, 4, 64, 128, 1000, 30, "full"),
+        LatentWorkload("latent_small_n8_b8_r128_h256_v32000", 8, 8, 128, 256, 32000, 31),
+        LatentWorkload("latent_ragged_n5_b12_r256_h512_v1000", 5, 12, 256, 512, 1000, 32),
+        LatentWorkload("latent_b32_n3_r128_h256_v1000", 3, 32, 128, 256, 1000, 33),
+        LatentWorkload("latent_n1_b16_r256_h512_v152064", 1, 16, 256, 512, 152064, 34),
+        LatentWorkload("latent_n64_b16_r256_h512_v152064", 64, 16, 256, 512, 152064, 35),
+        LatentWorkload("latent_n256_b16_r256_h512_v152064", 256, 16, 256, 512, 152064, 36),
+        LatentWorkload("latent_exact_n64_b16_r256_h512_v152064", 64, 16, 256, 512, 152064,
+                       37, "exact"),
+    ]
+}
+
+LATENT_BENCH_WORKLOAD = "latent_n256_b16_r256_h512_v152064"
+
+
+def generate_latent(w: LatentWorkload):
+    """Inputs of one latent pass, as a dict of numpy arrays.
+
+    Recipe (``SeedSequence(seed).spawn(4)``: id, cache, embedding and
+    layer-weight streams):
+      ids    blk [N, B] and am1 [N], uniform on [0, V) (int64);
+      cache  xh [N, B, R] ~ N(0, 1);
+      embed  w1 [V, R] ~ N(0, 1), then wlat [R, R] ~ N(0, 1/R);
+      layer  L [B, B, R] ~ N(0, 1/(4B)), then wg, wu [H, R] ~ N(0, 1/R) and
+             wd [R, H] ~ N(0, 1/H); the mixer is I + L, with L zeroed above
+             the diagonal for "causal".
+    For "exact": xh = 1 + k/128 with k uniform on [-64, 127]; w1 = k/16 and
+    wlat = k/16 with |k| <= 4 and <= 2; L = k/4 with |k| <= 2 below the
+    diagonal (zero on and above it); wg = wu = 0; wd ~ N(0, 1/H).  Every
+    projection sum is then a multiple of 2^-8, every mixer sum a multiple of
+    2^-10, all far inside fp32's 24 bits.
+    Float values become bf16 with round-to-nearest-even (torch, on the CPU).
+    Weight layouts are out-major (one row per output unit).
+    """
+    N, B, R, H, V = w.N, w.B, w.R, w.H, w.V
+    s_ids, s_xh, s_emb, s_layer = np.random.SeedSequence(w.seed).spawn(4)
+    gi = np.random.Generator(np.random.PCG64(s_ids))
+    blk = gi.integers(0, V, size=(N, B)).astype(np.int64)
+    am1 = gi.integers(0, V, size=N).astype(np.int64)
+    gx = np.random.Generator(np.random.PCG64(s_xh))
+    ge = np.random.Generator(np.random.PCG64(s_emb))
+    gl = np.random.Generator(np.random.PCG64(s_layer))
+    below = np.tril(np.ones((B, B), dtype=np.float32), -1)[:, :, None]
+    eye = np.eye(B, dtype=np.float32)[:, :, None]
+    if w.kind == "exact":
+        xh = 1.0 + gx.integers(-64, 128, size=(N, B, R)).astype(np.float32) / np.float32(128)
+        w1 = ge.integers(-4, 5, size=(V, R)).astype(np.float32) / np.float32(16)
+        wlat = ge.integers(-2, 3, size=(R, R)).astype(np.float32) / np.float32(16)
+        L = gl.integers(-2, 3, size=(B, B, R)).astype(np.float32) / np.float32(4)
+        mixl = eye + L * below
+        wg = np.zeros((H, R), dtype=np.float32)
+        wu = np.zeros((H, R), dtype=np.float32)
+        wd = gl.standard_normal((R, H), dtype=np.float32) / np.float32(np.sqrt(H))
+    else:
+        xh = gx.standard_normal((N, B, R), dtype=np.float32)
+        w1 = ge.standard_normal((V, R), dtype=np.float32)
+        wlat = ge.standard_normal((R, R), dtype=np.float32) / np.float32(np.sqrt(R))
+        L = gl.standard_normal((B, B, R), dtype=np.float32) / np.float32(np.sqrt(4 * B))
+        if w.kind == "causal":
+            L = L * (below + eye)
+        elif w.kind != "full":
+            raise ValueError("unknown latent workload kind %r" % w.kind)
+        mixl = eye + L
+        wg = gl.standard_normal((H, R), dtype=np.float32) / np.float32(np.sqrt(R))
+        wu = gl.standard_normal((H, R), dtype=np.float32) / np.float32(np.sqrt(R))
+        wd = gl.standard_normal((R, H), dtype=np.float32) / np.float32(np.sqrt(H))
+    return {
+        "blk": blk, "am1": am1,
+        "xh": f32_to_bf16_bits(xh), "w1": f32_to_bf16_bits(w1),
+        "wlat": f32_to_bf16_bits(wlat), "mixl": f32_to_bf16_bits(mixl),
+        "wg": f32_to_bf16_bits(wg), "wu": f32_to_bf16_bits(wu), "wd": f32_to_bf16_bits(wd),
+    }
