@@ -378,13 +378,110 @@ def bench_gemm(args, np, torch, native, workloads):
     return out
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, published
+
+
+def bench_latent(args, np, torch, native, workloads):
+    name = args.workload if (args.workload or "").startswith("latent_") else \
+        workloads.LATENT_BENCH_WORKLOAD
+    w = workloads.LATENT_WORKLOADS[name]
+    log("generating %s" % name)
+    d = workloads.generate_latent(w)
+    keys = ("blk", "am1", "xh", "w1", "wlat", "mixl", "wg", "wu", "wd")
+    dev = {k: torch.from_numpy(d[k].view(np.int16) if d[k].dtype == np.uint16 else d[k]).cuda()
+           for k in keys}
+    out_d = torch.empty((w.N, w.B - 1, w.R), dtype=torch.int16, device="cuda")
+    stream = torch.cuda.current_stream()
+    native.xpress_latent_reserve(w.N, w.B, w.R, w.H, stream=stream)
+
+    def step(k, st=stream):
+        native.xpress_latent_pass(*(dev[x] for x in keys), out_d, w.N, w.B, w.R, w.H, w.V,
+                                  stream=st)
+
+    if args.graph:
+        wall, region_gpu, n = time_graph(
+            step, args.steps, args.warmup, args.graph,
+            lambda st: native.xpress_latent_reserve(w.N, w.B, w.R, w.H, stream=st))
+        args.steps = n
+        durs = [region_gpu / n]
+    else:
+        wall, region_gpu, durs = time_steps(step, args.steps, args.warmup, stream)
+    got = out_d.cpu().numpy().view(np.uint16)
+    per_pass = region_gpu / args.steps
+    achieved = w.flops / per_pass / 1e12
+    out = {
+        "metric": "latent stage of one pass: blocks/s and us per pass, N=%d B=%d R=%d H=%d"
+                  % (w.N, w.B, w.R, w.H),
+        "value": round(w.N * args.steps / wall, 1),
+        "unit": "blocks/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "op": "latent", "N": w.N, "B": w.B, "R": w.R, "H": w.H,
+                   "V": w.V, "flops_per_step": w.flops, "bytes_per_step": w.bytes_moved,
+                   "launches_per_step": 3,
+                   "caches": "one input set: the ~1 MB of weights stay cache-resident",
+                   "launch": ("hip graph of %d steps" % args.graph) if args.graph else "stream"},
+        "us_per_pass": round(per_pass * 1e6, 3),
+        "pass_us_event_pairs": {"avg": round(sum(durs) / len(durs) * 1e6, 3),
+                                "min": round(durs[0] * 1e6, 3),
+                                "p50": round(durs[len(durs) // 2] * 1e6, 3)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 5), "traffic": None,
+                     "note": "three kernels per pass; achieved over the pass's GPU time"},
+        "cpu_baseline": None,
+    }
+
+    # context: the same stage as separate torch operations (gather, matmuls,
+    # mixer, SwiGLU), each its own launch
+    f32 = {k: dev[k].view(torch.bfloat16).float() for k in ("xh", "mixl")}
+    wb = {k: dev[k].view(torch.bfloat16) for k in ("w1", "wlat", "wg", "wu", "wd")}
+    wt = {k: wb[k].t().contiguous() for k in ("wlat", "wg", "wu", "wd")}
+    toks = torch.cat([dev["am1"].view(-1, 1), dev["blk"][:, :w.B - 1]], dim=1)
+
+    def torch_stage(k, st=stream):
+        emb = wb["w1"].index_select(0, toks.reshape(-1))
+        x = f32["xh"] + torch.matmul(emb, wt["wlat"]).float().view(w.N, w.B, w.R)
+        u = (f32["mixl"].unsqueeze(0) * x.unsqueeze(1)).sum(dim=2)[:, 1:].reshape(-1, w.R)
+        ub = u.to(torch.bfloat16)
+        g = torch.matmul(ub, wt["wg"]).float()
+        v = torch.matmul(ub, wt["wu"]).float()
+        m = (torch.nn.functional.silu(g) * v).to(torch.bfloat16)
+        return (u + torch.matmul(m, wt["wd"]).float()).to(torch.bfloat16)
+
+    tw, tg, _ = time_steps(torch_stage, max(50, args.steps // 5), max(20, args.warmup // 5),
+                           stream)
+    out["torch_ops_us_per_pass"] = round(tg / max(50, args.steps // 5) * 1e6, 2)
+    if not args.no_cpu_baseline:
+        import oracle
+        log("cpu baseline")
+        cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else 1
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            want = oracle.latent_pass(*(d[x] for x in keys), w.N, w.B, w.R, w.H, w.V,
+                                      threads=cores)
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= args.cpu_seconds or passes >= 1000:
+                break
+        out["cpu_baseline"] = {"value": round(passes * w.N / dt, 2), "unit": "blocks/s",
+                               "cores": cores, "kind": "oracle",
+                               "us_per_pass": round(dt / passes * 1e6, 1),
+                               "sample": "all %d blocks of %s, %d passes, %.1f s on %d threads"
+                                         % (w.N, name, passes, dt, cores)}
+        out["checked_equal_fraction"] = round(float(np.mean(got == want)), 5)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--op", choices=["readout", "topc", "gemm"], default="readout")
+    ap.add_argument("--op", choices=["readout", "topc", "gemm", "latent"], default="readout")
     ap.add_argument("--graph", type=int, default=0,
                     help="capture this many steps per HIP graph and time graph replays")
     ap.add_argument("--topc-c", type=int, default=1024, choices=[64, 256, 1024, 4096])
@@ -415,6 +512,8 @@ def main():
         out = bench_topc(args, np, torch, native, workloads)
     elif args.op == "gemm":
         out = bench_gemm(args, np, torch, native, workloads)
+    elif args.op == "latent":
+        out = bench_latent(args, np, torch, native, workloads)
     else:
         out = bench_readout(args, np, torch, native, workloads)
     print(json.dumps(out))

@@ -156,6 +156,70 @@ int xpress_readout_gemm_argmax_to_blk(const uint16_t* base, const uint16_t* x,
 int xpress_reserve(int64_t N, int64_t B, int64_t V, hipStream_t stream);
 
 /*
+ * xpress_latent_pass -- the latent stage of one Jacobi pass (XPress kernels
+ * page, module description and "_xpress_latent_kernel"), which produces the
+ * rows the readout matmul consumes.  For every block n and slot b:
+ *
+ *     prev[b]  = am1[n] for b = 0, blk[n, b-1] otherwise
+ *     x[b, :]  = xh[n, b, :] + w1[prev[b], :] @ wlat^T          (fp32)
+ *     u[b, r]  = sum_{j < B} mixl[b, j, r] * x[j, r]             (fp32)
+ *     g        = bf16(u[b]) @ wg^T,   v = bf16(u[b]) @ wu^T      (fp32)
+ *     m        = bf16( g * sigmoid(g) * v )                      (SwiGLU)
+ *     lat_out[n, b-1, :] = bf16( u[b] + m @ wd^T ),   b = 1 .. B-1
+ *
+ * Slot 0 is the verified anchor: its x enters the mixer of the later slots,
+ * but no latent is written for it.
+ *
+ *   blk      device pointer, int64 [N, B] row-major: the block's tokens; slot
+ *            b reads blk[n, b-1] (blk[n, B-1] is never read).  Read only.
+ *   am1      device pointer, int64 [N]: the token before each block's anchor.
+ *   xh       device pointer, bf16 [N, B, R]: the pass-invariant hidden cache.
+ *   w1       device pointer, bf16 [V, R]: token embedding, one row per id.
+ *   wlat     device pointer, bf16 [R, R]: embedding-to-latent projection,
+ *            out-major (row r holds the weights of output channel r).
+ *   mixl     device pointer, bf16 [B, B, R]: the folded mixer (L * tril + I)
+ *            per channel; every j < B is summed, so entries above the
+ *            diagonal must be zero for a causal mixer.
+ *   wg, wu   device pointers, bf16 [H, R]: SwiGLU gate and up, out-major.
+ *   wd       device pointer, bf16 [R, H]: SwiGLU down, out-major.
+ *   lat_out  device pointer, bf16 [N, B-1, R]: written whole.  Must not
+ *            overlap any input.
+ *   N        blocks, >= 0 (N * B <= 2^31 - 1).
+ *   B        slots per block, 2 .. 32.
+ *   R        latent rank, a multiple of 64 in [64, 1024].
+ *   H        MLP hidden size, a multiple of 64 in [64, 8192].
+ *   V        rows of w1, >= 1.
+ *   stream   HIP stream (0 = the null stream).
+ *
+ * xh, w1, wlat, mixl, wg, wu and wd must be 16-byte aligned; blk and am1
+ * 8-byte aligned.  A token id outside [0, V) reads as a zero embedding row (no
+ * out-of-bounds read; the result for that slot is then meaningless).  The
+ * fp32 accumulation order is the matrix cores'; results agree with the exact
+ * definition up to fp32 rounding of the sums before each bf16 rounding.
+ *
+ * Asynchronous; three launches on `stream`.  N == 0 queues nothing.  Uses the
+ * (device, stream) workspace for u, bf16(u) and m (rows * (6R + 2H) bytes,
+ * rows = N * (B-1)); grow it beforehand with xpress_latent_reserve when the
+ * call will be captured into a HIP graph.  Errors: XPRESS_EINVAL (sizes,
+ * alignment, null pointers, overlap; nothing queued), XPRESS_ENOMEM /
+ * XPRESS_ECAPTURE (workspace), XPRESS_EHIP (launch).
+ */
+int xpress_latent_pass(const int64_t* blk, const int64_t* am1, const uint16_t* xh,
+                       const uint16_t* w1, const uint16_t* wlat, const uint16_t* mixl,
+                       const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
+                       uint16_t* lat_out, int64_t N, int64_t B, int64_t R, int64_t H,
+                       int64_t V, hipStream_t stream);
+
+/*
+ * xpress_latent_reserve -- grow the (device, stream) workspace to what
+ * xpress_latent_pass needs for (N, B, R, H), so that a captured call
+ * allocates nothing.  Synchronous.  Returns XPRESS_OK, XPRESS_EINVAL,
+ * XPRESS_ENOMEM or XPRESS_EHIP.  Growing the workspace later (a larger shape
+ * on the same stream) invalidates graphs captured before.
+ */
+int xpress_latent_reserve(int64_t N, int64_t B, int64_t R, int64_t H, hipStream_t stream);
+
+/*
  * xpress_release -- free every workspace the library holds on the current
  * device (after synchronising that device).  Optional; for tests and for
  * callers that want the memory back.

@@ -76,6 +76,8 @@ def _load():
             _U16P, _U16P, _U16P, _I64P] + [ctypes.c_int64] * 5
         lib.oracle_gemm_argmax_rows.restype = ctypes.c_int
         _DP = ctypes.POINTER(ctypes.c_double)
+        lib.oracle_bf16_from_double_many.argtypes = [_DP, _U16P, ctypes.c_int64]
+        lib.oracle_bf16_from_double_many.restype = None
         lib.oracle_latent_pass.argtypes = (
             [_I64P, _I64P] + [_U16P] * 7 + [_U16P] + [ctypes.c_int64] * 5 + [_DP] * 6)
         lib.oracle_latent_pass.restype = ctypes.c_int
@@ -102,6 +104,16 @@ def bf16_to_double(h: int) -> float:
 def bf16_from_double(x: float) -> int:
     """Nearest bf16 (ties to even) of a binary64 value, as a bit pattern."""
     return int(_load().oracle_bf16_from_double(float(x)))
+
+
+def bf16_from_double_many(x) -> np.ndarray:
+    """bf16 patterns (uint16) of float64 values, each rounded once to nearest
+    even; same shape as x."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().oracle_bf16_from_double_many(
+        x.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), _p16(out), x.size)
+    return out
 
 
 def bf16_sum(a: int, b: int) -> int:

@@ -128,6 +128,14 @@ uint16_t oracle_bf16_from_double(double x)
 }
 
 /* The rounded sum of one pair: bf16(a + b), formed in binary64. */
+/* Element-wise oracle_bf16_from_double over n values. */
+void oracle_bf16_from_double_many(const double* x, uint16_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        out[i] = oracle_bf16_from_double(x[i]);
+    }
+}
+
 uint16_t oracle_bf16_sum(uint16_t a, uint16_t b)
 {
     double s = oracle_bf16_to_double(a) + oracle_bf16_to_double(b);

@@ -159,3 +159,44 @@ def test_gemm_no_rows_is_ok_without_pointers():
     lib = native.load()
     assert lib.xpress_readout_gemm_argmax_to_blk(0, 0, 0, 0, 0, 16, 152064, 256, 152064,
                                                  None) == 0
+
+
+# latent pass: blk, am1, xh, w1, wlat, mixl, wg, wu, wd, lat_out, N, B, R, H, V
+_LAT_PTRS = [0x10000, 0x20000, 0x30000, 0x100000, 0x200000, 0x300000, 0x400000, 0x500000,
+             0x600000, 0x700000]
+
+
+def _lat(ptr_changes=None, **sizes):
+    ptrs = list(_LAT_PTRS)
+    for i, p in (ptr_changes or {}).items():
+        ptrs[i] = p
+    dims = dict(N=1, B=4, R=64, H=64, V=8)
+    dims.update(sizes)
+    return tuple(ptrs) + (dims["N"], dims["B"], dims["R"], dims["H"], dims["V"])
+
+
+@no_gpu_only
+@pytest.mark.parametrize("args", [
+    _lat(N=-1), _lat(B=1), _lat(B=33), _lat(R=96), _lat(R=32), _lat(R=2048),
+    _lat(H=96), _lat(H=16384), _lat(V=0), _lat(N=2 ** 30, B=4),
+    _lat({2: 0}),                 # null xh
+    _lat({0: 0}),                 # null blk
+    _lat({9: 0}),                 # null lat_out
+    _lat({3: 0x100008}),          # w1 not 16-byte aligned
+    _lat({6: 0x400004}),          # wg not 16-byte aligned
+    _lat({1: 0x20004}),           # am1 not 8-byte aligned
+    _lat({9: 0x30000}),           # lat_out overlaps xh
+    _lat({9: 0x100200}),          # lat_out inside w1 (1 KiB at 0x100000)
+    _lat({9: 0x0FFFE}),           # lat_out runs into blk
+])
+def test_latent_invalid_arguments_rejected_before_launch(args):
+    lib = native.load()
+    assert lib.xpress_latent_pass(*args, None) == native.XPRESS_EINVAL
+
+
+@no_gpu_only
+def test_latent_no_blocks_is_ok_without_pointers():
+    lib = native.load()
+    assert lib.xpress_latent_pass(*([0] * 10), 0, 16, 256, 512, 152064, None) == 0
+    assert lib.xpress_latent_reserve(0, 16, 256, 512, None) == 0
+    assert lib.xpress_latent_reserve(1, 16, 96, 512, None) == native.XPRESS_EINVAL

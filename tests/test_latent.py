@@ -1,0 +1,159 @@
+"""Parity of the HIP latent stage (xpress_latent_pass) with the CPU oracle.
+
+The GPU forms every sum in fp32 in the matrix cores' order; the oracle forms
+the exact values.  The bar, per workload:
+  * every output element lies in the acceptance interval of
+    tests/latent_bound.py: the bf16 roundings of [O - E, O + E], where O is
+    the oracle's exact pre-rounding output and E bounds (worst case) what fp32
+    rounding of the sums, and the bf16 roundings it can tip, move it;
+  * at least 99% of the elements equal the oracle's bit for bit (fp32
+    emulation of the stage on the CPU gives 99.7-99.9%; a misplaced rounding
+    -- an unrounded u or m, a rounded residual, a truncating conversion --
+    drops this to 80-95%);
+  * "exact" workloads (every fp32 sum exact, the MLP adding exactly 0): bit
+    for bit equal; "mlp_dyadic" (x, u, g, v exact): the interval is computed
+    with those stages exact, which leaves one or two admissible values for
+    almost every element.
+"""
+import numpy as np
+import pytest
+
+from conftest import gpu_available
+from gpu_util import say, to_dev, ORACLE_THREADS
+import latent_bound
+import oracle
+from vocab_wide_add_amd import native, workloads
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+KEYS = ("blk", "am1", "xh", "w1", "wlat", "mixl", "wg", "wu", "wd")
+
+
+def dev_inputs(d):
+    return {k: to_dev(d[k]) for k in KEYS}
+
+
+def gpu_latent(dd, N, B, R, H, V, stream=None):
+    import torch
+    out = torch.empty((N, B - 1, R), dtype=torch.int16, device="cuda")
+    out.fill_(-1)
+    native.xpress_latent_pass(*(dd[k] for k in KEYS), out, N, B, R, H, V, stream=stream)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().view(np.uint16)
+
+
+def oracle_latent(d, N, B, R, H, V):
+    return oracle.latent_pass(*(d[k] for k in KEYS), N, B, R, H, V, intermediates=True,
+                              threads=ORACLE_THREADS)
+
+
+def assert_parity(got, want, d, inter, B, R, H, kind):
+    if kind == "exact":
+        assert np.array_equal(got, want), np.argwhere(got != want)[:5]
+        return
+    through = "gv" if kind == "mlp_dyadic" else ""
+    ok, exact, worst = latent_bound.check(got, want, d, inter, B, R, H, through)
+    say("  exact fraction %.5f" % exact)
+    assert ok, worst
+    assert exact >= 0.99, exact
+
+
+@pytest.mark.parametrize("name", list(workloads.LATENT_WORKLOADS))
+def test_latent_workload(name):
+    w = workloads.LATENT_WORKLOADS[name]
+    d = workloads.generate_latent(w)
+    want, inter = oracle_latent(d, w.N, w.B, w.R, w.H, w.V)
+    say("latent %s" % name)
+    got = gpu_latent(dev_inputs(d), w.N, w.B, w.R, w.H, w.V)
+    assert_parity(got, want, d, inter, w.B, w.R, w.H, w.kind)
+
+
+@pytest.mark.parametrize("N,B,R,H", [(1, 2, 64, 64), (3, 3, 64, 192), (7, 5, 128, 64),
+                                     (33, 16, 192, 128), (2, 31, 64, 64), (1, 32, 64, 64)])
+def test_latent_shapes(N, B, R, H):
+    """Ragged tiles: blocks per tile = 32 // B, row tiles that end mid-tile,
+    channel and hidden counts that are not powers of two."""
+    V = 50
+    w = workloads.LatentWorkload("adhoc", N, B, R, H, V, seed=1000 + N * B + R + H)
+    d = workloads.generate_latent(w)
+    want, inter = oracle_latent(d, N, B, R, H, V)
+    say("latent shape N=%d B=%d R=%d H=%d" % (N, B, R, H))
+    got = gpu_latent(dev_inputs(d), N, B, R, H, V)
+    assert_parity(got, want, d, inter, B, R, H, "causal")
+
+
+def test_latent_no_blocks_and_errors():
+    import torch
+    w = workloads.LATENT_WORKLOADS["latent_tiny_n2_b4_r64_h128_v1000"]
+    d = workloads.generate_latent(w)
+    dd = dev_inputs(d)
+    out = torch.full((w.N, w.B - 1, w.R), 7, dtype=torch.int16, device="cuda")
+    say("latent N=0")
+    native.xpress_latent_pass(*(dd[k] for k in KEYS), out, 0, w.B, w.R, w.H, w.V)
+    torch.cuda.synchronize()
+    assert (out == 7).all()
+    # misaligned weight, bad sizes, output overlapping an input: rejected
+    bad = dict(dd)
+    bad["wg"] = dd["wg"].view(-1)[1:]
+    with pytest.raises(native.XpressError):
+        native.xpress_latent_pass(*(bad[k] for k in KEYS), out, w.N, w.B, w.R, w.H, w.V)
+    with pytest.raises(native.XpressError):
+        native.xpress_latent_pass(*(dd[k] for k in KEYS), out, w.N, w.B, 96, w.H, w.V)
+    with pytest.raises(native.XpressError):
+        native.xpress_latent_pass(*(dd[k] for k in KEYS), dd["xh"], w.N, w.B, w.R, w.H, w.V)
+    torch.cuda.synchronize()
+    assert (out == 7).all()
+
+
+def test_latent_out_of_range_id_reads_zero_embedding():
+    """An id outside [0, V) is read as a zero embedding row: the oracle with
+    an extra all-zero row V of w1 and that id set to V gives the answer."""
+    w = workloads.LATENT_WORKLOADS["latent_small_n8_b8_r128_h256_v32000"]
+    d = workloads.generate_latent(w)
+    d["am1"][2] = w.V + 5
+    d["blk"][3, 1] = -4
+    dd = dev_inputs(d)
+    e = dict(d)
+    e["w1"] = np.concatenate([d["w1"], np.zeros((1, w.R), dtype=np.uint16)])
+    e["am1"] = d["am1"].copy()
+    e["blk"] = d["blk"].copy()
+    e["am1"][2] = w.V
+    e["blk"][3, 1] = w.V
+    want, inter = oracle_latent(e, w.N, w.B, w.R, w.H, w.V + 1)
+    say("latent out-of-range ids")
+    got = gpu_latent(dd, w.N, w.B, w.R, w.H, w.V)
+    assert_parity(got, want, e, inter, w.B, w.R, w.H, "causal")
+
+
+def test_latent_repeat_streams_and_graph():
+    """Same answer on a second stream, after a larger call grew the
+    workspace, and on every replay of a captured graph."""
+    import torch
+    w = workloads.LATENT_WORKLOADS["latent_n64_b16_r256_h512_v152064"]
+    d = workloads.generate_latent(w)
+    dd = dev_inputs(d)
+    say("latent repeat / stream / graph")
+    first = gpu_latent(dd, w.N, w.B, w.R, w.H, w.V)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        second = gpu_latent(dd, w.N, w.B, w.R, w.H, w.V, stream=s)
+    assert np.array_equal(first, second)
+    # a smaller call after the large one reuses the workspace
+    small = gpu_latent(dd, 5, w.B, w.R, w.H, w.V)
+    assert np.array_equal(small, first[:5])
+    # graph: reserve, capture, replay several times with eager work between
+    out = torch.empty((w.N, w.B - 1, w.R), dtype=torch.int16, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    gs = torch.cuda.Stream()
+    native.xpress_latent_reserve(w.N, w.B, w.R, w.H, stream=gs)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=gs):
+        native.xpress_latent_pass(*(dd[k] for k in KEYS), out, w.N, w.B, w.R, w.H, w.V,
+                                  stream=gs)
+    for i in range(3):
+        out.fill_(i)
+        gpu_latent(dd, 3, w.B, w.R, w.H, w.V)  # eager work in between
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint16), first), i

@@ -236,3 +236,15 @@ def test_workload_recipes_match_their_kind():
     w = workloads.LATENT_WORKLOADS["latent_exact_n64_b16_r256_h512_v152064"]
     d = workloads.generate_latent(w)
     assert not d["wg"].any() and not d["wu"].any()
+
+
+def test_vector_rounding_matches_the_pinned_scalar_rounding():
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.standard_normal(2000) * 10.0 ** rng.integers(-40, 40, 2000),
+                        [0.0, -0.0, 1e300, -1e300, 2.0 ** -134, 3 * 2.0 ** -134, 1.00390625]])
+    got = oracle.bf16_from_double_many(x)
+    assert got.shape == x.shape
+    assert all(int(g) == oracle.bf16_from_double(float(v)) for g, v in zip(got, x))
+    # and the exact-search rounding agrees on the finite ones
+    for g, v in zip(got[:200], x[:200]):
+        assert int(g) == exact_bf16.round_exact(Fraction(float(v)))

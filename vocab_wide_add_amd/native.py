@@ -62,6 +62,10 @@ def load():
         lib.xpress_readout_gemm_argmax_to_blk.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64,
                                                           i64, vp]
         lib.xpress_readout_gemm_argmax_to_blk.restype = i32
+        lib.xpress_latent_pass.argtypes = [vp] * 10 + [i64] * 5 + [vp]
+        lib.xpress_latent_pass.restype = i32
+        lib.xpress_latent_reserve.argtypes = [i64, i64, i64, i64, vp]
+        lib.xpress_latent_reserve.restype = i32
         lib.xpress_reserve.argtypes = [i64, i64, i64, vp]
         lib.xpress_reserve.restype = i32
         lib.xpress_release.argtypes = []
@@ -144,6 +148,24 @@ def xpress_readout_gemm_argmax_to_blk(base, x, w, blk, N: int, B: int, V: int, R
                                                  int(N), int(B), int(V), int(R),
                                                  int(stride_base_r), _stream(stream)),
            "xpress_readout_gemm_argmax_to_blk")
+
+
+def xpress_latent_pass(blk, am1, xh, w1, wlat, mixl, wg, wu, wd, lat_out, N: int, B: int,
+                       R: int, H: int, V: int, stream=None) -> None:
+    """Latent stage of one pass: lat_out [N, B-1, R] from the block tokens
+    blk [N, B], am1 [N] (int64), the hidden cache xh [N, B, R], the embedding
+    w1 [V, R] and the out-major weights wlat [R, R], mixl [B, B, R],
+    wg / wu [H, R], wd [R, H] (all bf16 on the GPU)."""
+    lib = load()
+    _check(lib.xpress_latent_pass(_ptr(blk), _ptr(am1), _ptr(xh), _ptr(w1), _ptr(wlat),
+                                  _ptr(mixl), _ptr(wg), _ptr(wu), _ptr(wd), _ptr(lat_out),
+                                  int(N), int(B), int(R), int(H), int(V), _stream(stream)),
+           "xpress_latent_pass")
+
+
+def xpress_latent_reserve(N: int, B: int, R: int, H: int, stream=None) -> None:
+    _check(load().xpress_latent_reserve(int(N), int(B), int(R), int(H), _stream(stream)),
+           "xpress_latent_reserve")
 
 
 def xpress_reserve(N: int, B: int, V: int, stream=None) -> None:

@@ -343,7 +343,10 @@ class LatentWorkload:
     # "full":   mixer = I + L everywhere (checks that every slot is summed);
     # "exact":  dyadic values and wg = wu = 0, so every fp32 sum is exact,
     #           the MLP adds exactly 0 and the output is bf16(u) with many
-    #           exact ties.
+    #           exact ties;
+    # "mlp_dyadic": wlat = 0 and mixer = I, so u = xh, with xh, wg, wu on
+    #           coarse dyadic grids: x, u, g and v are exact in fp32 and only
+    #           the SwiGLU, m and the down projection round.
     kind: str = "causal"
 
     @property
@@ -386,6 +389,8 @@ LATENT_WORKLOADS = {
         LatentWorkload("latent_n256_b16_r256_h512_v152064", 256, 16, 256, 512, 152064, 36),
         LatentWorkload("latent_exact_n64_b16_r256_h512_v152064", 64, 16, 256, 512, 152064,
                        37, "exact"),
+        LatentWorkload("latent_mlp_dyadic_n64_b16_r256_h512_v152064", 64, 16, 256, 512,
+                       152064, 38, "mlp_dyadic"),
     ]
 }
 
@@ -408,6 +413,10 @@ def generate_latent(w: LatentWorkload):
     diagonal (zero on and above it); wg = wu = 0; wd ~ N(0, 1/H).  Every
     projection sum is then a multiple of 2^-8, every mixer sum a multiple of
     2^-10, all far inside fp32's 24 bits.
+    For "mlp_dyadic": xh = k/8 with |k| <= 16, wlat = 0, mixer = I,
+    wg = wu = k/64 with |k| <= 8, wd ~ N(0, 1/H) (w1 as usual): every gate and
+    up product is a multiple of 2^-9 of magnitude <= 1/4, so with R <= 1024
+    every partial sum is a multiple of 2^-9 below 2^8, exact in fp32.
     Float values become bf16 with round-to-nearest-even (torch, on the CPU).
     Weight layouts are out-major (one row per output unit).
     """
@@ -429,6 +438,14 @@ def generate_latent(w: LatentWorkload):
         mixl = eye + L * below
         wg = np.zeros((H, R), dtype=np.float32)
         wu = np.zeros((H, R), dtype=np.float32)
+        wd = gl.standard_normal((R, H), dtype=np.float32) / np.float32(np.sqrt(H))
+    elif w.kind == "mlp_dyadic":
+        xh = gx.integers(-16, 17, size=(N, B, R)).astype(np.float32) / np.float32(8)
+        w1 = ge.standard_normal((V, R), dtype=np.float32)
+        wlat = np.zeros((R, R), dtype=np.float32)
+        mixl = np.broadcast_to(eye, (B, B, R)).copy()
+        wg = gl.integers(-8, 9, size=(H, R)).astype(np.float32) / np.float32(64)
+        wu = gl.integers(-8, 9, size=(H, R)).astype(np.float32) / np.float32(64)
         wd = gl.standard_normal((R, H), dtype=np.float32) / np.float32(np.sqrt(H))
     else:
         xh = gx.standard_normal((N, B, R), dtype=np.float32)
