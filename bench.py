@@ -393,6 +393,8 @@ def bench_latent(args, np, torch, native, workloads):
     out_d = torch.empty((w.N, w.B - 1, w.R), dtype=torch.int16, device="cuda")
     stream = torch.cuda.current_stream()
     native.xpress_latent_reserve(w.N, w.B, w.R, w.H, stream=stream)
+    tiles = tuple(int(t) for t in args.latent_tiles.split(","))
+    native.xpress_latent_set_tiles(*tiles)
 
     def step(k, st=stream):
         native.xpress_latent_pass(*(dev[x] for x in keys), out_d, w.N, w.B, w.R, w.H, w.V,
@@ -420,7 +422,7 @@ def bench_latent(args, np, torch, native, workloads):
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": name, "op": "latent", "N": w.N, "B": w.B, "R": w.R, "H": w.H,
                    "V": w.V, "flops_per_step": w.flops, "bytes_per_step": w.bytes_moved,
-                   "launches_per_step": 3,
+                   "launches_per_step": 3, "tiles": args.latent_tiles,
                    "caches": "one input set: the ~1 MB of weights stay cache-resident",
                    "launch": ("hip graph of %d steps" % args.graph) if args.graph else "stream"},
         "us_per_pass": round(per_pass * 1e6, 3),
@@ -485,6 +487,8 @@ def main():
     ap.add_argument("--graph", type=int, default=0,
                     help="capture this many steps per HIP graph and time graph replays")
     ap.add_argument("--topc-c", type=int, default=1024, choices=[64, 256, 1024, 4096])
+    ap.add_argument("--latent-tiles", default="0,0,0",
+                    help="row-slab counts of the mix, gate and down kernels (0 = automatic)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU work budget of the oracle baseline leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -220,6 +220,22 @@ int xpress_latent_pass(const int64_t* blk, const int64_t* am1, const uint16_t* x
 int xpress_latent_reserve(int64_t N, int64_t B, int64_t R, int64_t H, hipStream_t stream);
 
 /*
+ * xpress_latent_set_tiles -- workgroup shape override for the three latent
+ * kernels, for tests and tuning.  Each workgroup computes 32 * slabs rows of
+ * a 32-column tile with its four waves; slabs = 4 gives every wave its own
+ * 32-row slab over the whole contraction, slabs = 2 or 1 split the
+ * contraction over 2 or 4 waves and sum the partials in LDS; 8 selects the
+ * LDS-staged kernels (128 rows per workgroup, operands copied to LDS in
+ * coalesced 64-wide contraction chunks, one chunk ahead).  Arguments are the
+ * choices for the mix, gate and down kernels: 1, 2, 4 or 8, or 0 for the
+ * library's choice per shape (staged from 2048 rows on, else the most slabs
+ * that still give each compute unit a workgroup).  Results are identical up
+ * to fp32 summation order.
+ * Process-wide; returns XPRESS_OK or XPRESS_EINVAL.
+ */
+int xpress_latent_set_tiles(int mix, int gate, int down);
+
+/*
  * xpress_release -- free every workspace the library holds on the current
  * device (after synchronising that device).  Optional; for tests and for
  * callers that want the memory back.

@@ -17,7 +17,7 @@ intermediates and the magnitudes of the inputs:
     rounds into [bf16(a - e), bf16(a + e)];
   * silu(g) * v changes by at most 1.1 * |v| per unit of g (the derivative of
     g * sigmoid(g) lies in [-0.1, 1.1]) and |g| per unit of v, and its fp32
-    evaluation (exp, add, divide, multiply) adds at most 64 fp32 ulps of
+    evaluation (exp, add, reciprocal, two multiplies) adds at most 64 fp32 ulps of
     relative error, plus 1e-30 absolute for underflow.
 
 The stages, with X, U, G, V, F, O the oracle's exact values:

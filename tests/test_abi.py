@@ -200,3 +200,16 @@ def test_latent_no_blocks_is_ok_without_pointers():
     assert lib.xpress_latent_pass(*([0] * 10), 0, 16, 256, 512, 152064, None) == 0
     assert lib.xpress_latent_reserve(0, 16, 256, 512, None) == 0
     assert lib.xpress_latent_reserve(1, 16, 96, 512, None) == native.XPRESS_EINVAL
+
+
+def test_latent_tile_override_validates():
+    try:
+        native.xpress_latent_set_tiles(1, 2, 4)
+        native.xpress_latent_set_tiles(8, 8, 8)
+        native.xpress_latent_set_tiles(0, 0, 0)
+        with pytest.raises(native.XpressError):
+            native.xpress_latent_set_tiles(3, 0, 0)
+        with pytest.raises(native.XpressError):
+            native.xpress_latent_set_tiles(0, 16, 0)
+    finally:
+        native.xpress_latent_set_tiles(0, 0, 0)

@@ -69,18 +69,49 @@ def test_latent_workload(name):
     assert_parity(got, want, d, inter, w.B, w.R, w.H, w.kind)
 
 
-@pytest.mark.parametrize("N,B,R,H", [(1, 2, 64, 64), (3, 3, 64, 192), (7, 5, 128, 64),
-                                     (33, 16, 192, 128), (2, 31, 64, 64), (1, 32, 64, 64)])
-def test_latent_shapes(N, B, R, H):
-    """Ragged tiles: blocks per tile = 32 // B, row tiles that end mid-tile,
-    channel and hidden counts that are not powers of two."""
+class Tiles:
+    """Force the latent kernels' row-slab counts for a block of code."""
+
+    def __init__(self, mix, gate, down):
+        self.t = (mix, gate, down)
+
+    def __enter__(self):
+        native.xpress_latent_set_tiles(*self.t)
+
+    def __exit__(self, *exc):
+        native.xpress_latent_set_tiles(0, 0, 0)
+
+
+SHAPES = [(1, 2, 64, 64), (3, 3, 64, 192), (7, 5, 128, 64), (33, 16, 192, 128),
+          (2, 31, 64, 64), (1, 32, 64, 64), (21, 7, 320, 576), (40, 16, 256, 512)]
+
+
+@pytest.mark.parametrize("tiles", [(1, 1, 1), (2, 2, 2), (4, 4, 4), (8, 8, 8)])
+@pytest.mark.parametrize("N,B,R,H", SHAPES)
+def test_latent_shapes(N, B, R, H, tiles):
+    """Every workgroup shape (8 = the LDS-staged kernels) on ragged tiles:
+    blocks per tile = 32*slabs // B (128 // B staged),
+    row tiles that end mid-slab, contractions that leave a remainder after
+    whole 4-step chunks (R/16 or H/16 per wave not a multiple of 4)."""
     V = 50
     w = workloads.LatentWorkload("adhoc", N, B, R, H, V, seed=1000 + N * B + R + H)
     d = workloads.generate_latent(w)
     want, inter = oracle_latent(d, N, B, R, H, V)
-    say("latent shape N=%d B=%d R=%d H=%d" % (N, B, R, H))
-    got = gpu_latent(dev_inputs(d), N, B, R, H, V)
+    say("latent shape N=%d B=%d R=%d H=%d tiles=%s" % (N, B, R, H, tiles))
+    with Tiles(*tiles):
+        got = gpu_latent(dev_inputs(d), N, B, R, H, V)
     assert_parity(got, want, d, inter, B, R, H, "causal")
+
+
+@pytest.mark.parametrize("tiles", [(1, 1, 1), (4, 4, 4), (8, 8, 8)])
+def test_latent_large_with_forced_tiles(tiles):
+    w = workloads.LATENT_WORKLOADS["latent_n256_b16_r256_h512_v152064"]
+    d = workloads.generate_latent(w)
+    want, inter = oracle_latent(d, w.N, w.B, w.R, w.H, w.V)
+    say("latent %s tiles=%s" % (w.name, tiles))
+    with Tiles(*tiles):
+        got = gpu_latent(dev_inputs(d), w.N, w.B, w.R, w.H, w.V)
+    assert_parity(got, want, d, inter, w.B, w.R, w.H, w.kind)
 
 
 def test_latent_no_blocks_and_errors():
@@ -126,34 +157,36 @@ def test_latent_out_of_range_id_reads_zero_embedding():
     assert_parity(got, want, e, inter, w.B, w.R, w.H, "causal")
 
 
-def test_latent_repeat_streams_and_graph():
-    """Same answer on a second stream, after a larger call grew the
-    workspace, and on every replay of a captured graph."""
+@pytest.mark.parametrize("tiles", [(1, 1, 1), (8, 8, 8)])
+def test_latent_repeat_streams_and_graph(tiles):
+    """With one workgroup shape throughout (each row's arithmetic is then
+    fixed): the same answer on a second stream, from a smaller call after a
+    larger one grew the workspace, and on every replay of a captured graph."""
     import torch
     w = workloads.LATENT_WORKLOADS["latent_n64_b16_r256_h512_v152064"]
     d = workloads.generate_latent(w)
     dd = dev_inputs(d)
-    say("latent repeat / stream / graph")
-    first = gpu_latent(dd, w.N, w.B, w.R, w.H, w.V)
-    s = torch.cuda.Stream()
-    with torch.cuda.stream(s):
-        second = gpu_latent(dd, w.N, w.B, w.R, w.H, w.V, stream=s)
-    assert np.array_equal(first, second)
-    # a smaller call after the large one reuses the workspace
-    small = gpu_latent(dd, 5, w.B, w.R, w.H, w.V)
-    assert np.array_equal(small, first[:5])
-    # graph: reserve, capture, replay several times with eager work between
-    out = torch.empty((w.N, w.B - 1, w.R), dtype=torch.int16, device="cuda")
-    g = torch.cuda.CUDAGraph()
-    gs = torch.cuda.Stream()
-    native.xpress_latent_reserve(w.N, w.B, w.R, w.H, stream=gs)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(g, stream=gs):
-        native.xpress_latent_pass(*(dd[k] for k in KEYS), out, w.N, w.B, w.R, w.H, w.V,
-                                  stream=gs)
-    for i in range(3):
-        out.fill_(i)
-        gpu_latent(dd, 3, w.B, w.R, w.H, w.V)  # eager work in between
-        g.replay()
+    say("latent repeat / stream / graph tiles=%s" % (tiles,))
+    with Tiles(*tiles):
+        first = gpu_latent(dd, w.N, w.B, w.R, w.H, w.V)
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            second = gpu_latent(dd, w.N, w.B, w.R, w.H, w.V, stream=s)
+        assert np.array_equal(first, second)
+        small = gpu_latent(dd, 5, w.B, w.R, w.H, w.V)
+        assert np.array_equal(small, first[:5])
+        # graph: reserve, capture, replay several times with eager work between
+        out = torch.empty((w.N, w.B - 1, w.R), dtype=torch.int16, device="cuda")
+        g = torch.cuda.CUDAGraph()
+        gs = torch.cuda.Stream()
+        native.xpress_latent_reserve(w.N, w.B, w.R, w.H, stream=gs)
         torch.cuda.synchronize()
-        assert np.array_equal(out.cpu().numpy().view(np.uint16), first), i
+        with torch.cuda.graph(g, stream=gs):
+            native.xpress_latent_pass(*(dd[k] for k in KEYS), out, w.N, w.B, w.R, w.H, w.V,
+                                      stream=gs)
+        for i in range(3):
+            out.fill_(i)
+            gpu_latent(dd, 3, w.B, w.R, w.H, w.V)  # eager work in between
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(out.cpu().numpy().view(np.uint16), first), i

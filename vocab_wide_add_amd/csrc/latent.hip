@@ -43,6 +43,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "device_common.h"
 #include "host_common.h"
 #include "xpress_argmax.h"
@@ -55,20 +57,15 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kTile = 32;      // rows and columns of one MFMA tile
-constexpr int kWaves = 4;      // waves of a workgroup; they split K
+constexpr int kWaves = 4;      // waves of a workgroup
 constexpr int kThreads = kWaves * 64;
-constexpr int kChunk = 4;      // MFMA k-steps whose operands are loaded at once
+constexpr int kChunk = 4;      // MFMA k-steps whose operands are loaded together
 constexpr int kMaxB = 32;
-constexpr int kPad = kTile + 1;  // LDS row stride of a 32 x 32 fp32 tile
+constexpr int kPad = kTile + 1;  // LDS row stride of a 32-column fp32 tile
 
-__device__ __forceinline__ bf16x8 load8(const uint16_t* p)
+__device__ __forceinline__ u32x4 load16(const uint16_t* p)
 {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
-}
-
-__device__ __forceinline__ bf16x8 zero8()
-{
-    return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    return *reinterpret_cast<const u32x4*>(p);
 }
 
 __device__ __forceinline__ uint16_t to_bf16(float x)
@@ -78,38 +75,132 @@ __device__ __forceinline__ uint16_t to_bf16(float x)
 
 __device__ __forceinline__ float from_bf16(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// acc += A[32 x K] * B[K x 32] over this wave's K range [k_begin, k_begin +
-// k_len), k_len a multiple of 16.  a_row / b_row point at the row (of A) and
-// the column (of B, stored as a row of the out-major weight) this lane
-// supplies, or a_row is null for a padding row (zeros).
-__device__ __forceinline__ void mfma_range(f32x16& acc, const uint16_t* a_row,
-                                           const uint16_t* b_row, int k_begin, int k_len,
-                                           int half)
+// Operands of kChunk MFMA k-steps: A (8 k-values of this lane's row) and NB
+// B operands sharing it (8 k-values of this lane's column of each weight).
+template <int NB>
+struct Chunk {
+    u32x4 a[kChunk];
+    u32x4 b[NB][kChunk];
+};
+
+// ap / bp point at k = 0 of this lane's row (A) and columns (B), already
+// offset by 8 * (lane / 32); amask zeroes A (a zero embedding row).
+template <int NB>
+__device__ __forceinline__ void load_chunk(Chunk<NB>& c, const uint16_t* ap,
+                                           const uint16_t* const (&bp)[NB], int k, uint32_t amask)
 {
-    for (int k0 = 0; k0 < k_len; k0 += 16 * kChunk) {
-        bf16x8 a[kChunk], b[kChunk];
 #pragma unroll
-        for (int s = 0; s < kChunk; ++s) {
-            const int k = k_begin + k0 + 16 * s + 8 * half;
-            const bool live = k0 + 16 * s < k_len;
-            a[s] = (live && a_row) ? load8(a_row + k) : zero8();
-            b[s] = live ? load8(b_row + k) : zero8();
-        }
+    for (int s = 0; s < kChunk; ++s) {
+        c.a[s] = load16(ap + k + 16 * s) & amask;
 #pragma unroll
-        for (int s = 0; s < kChunk; ++s) {
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b[s], acc, 0, 0, 0);
+        for (int m = 0; m < NB; ++m) c.b[m][s] = load16(bp[m] + k + 16 * s);
+    }
+}
+
+template <int NB>
+__device__ __forceinline__ void mma_chunk(f32x16 (&acc)[NB], const Chunk<NB>& c)
+{
+#pragma unroll
+    for (int s = 0; s < kChunk; ++s) {
+#pragma unroll
+        for (int m = 0; m < NB; ++m) {
+            acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, c.a[s]), __builtin_bit_cast(bf16x8, c.b[m][s]),
+                acc[m], 0, 0, 0);
         }
     }
 }
 
+// acc[m] += A[32 x K] * B_m[K x 32] over k = k0 .. k0 + 16 * steps, in
+// chunks of kChunk steps whose loads are issued one chunk ahead (two register
+// buffers), then the remaining single steps.
+template <int NB>
+__device__ __forceinline__ void mma_k(f32x16 (&acc)[NB], const uint16_t* ap,
+                                      const uint16_t* const (&bp)[NB], int k0, int steps,
+                                      uint32_t amask)
+{
+    const int nfull = steps / kChunk;
+    Chunk<NB> c0, c1;
+    int c = 0;
+    if (nfull > 0) load_chunk(c0, ap, bp, k0, amask);
+    for (; c + 2 <= nfull; c += 2) {
+        load_chunk(c1, ap, bp, k0 + 16 * kChunk * (c + 1), amask);
+        mma_chunk(acc, c0);
+        if (c + 2 < nfull) load_chunk(c0, ap, bp, k0 + 16 * kChunk * (c + 2), amask);
+        mma_chunk(acc, c1);
+    }
+    if (c < nfull) mma_chunk(acc, c0);
+    for (int s = nfull * kChunk; s < steps; ++s) {
+        const u32x4 av = load16(ap + k0 + 16 * s) & amask;
+#pragma unroll
+        for (int m = 0; m < NB; ++m) {
+            acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, av),
+                __builtin_bit_cast(bf16x8, load16(bp[m] + k0 + 16 * s)), acc[m], 0, 0, 0);
+        }
+    }
+}
+
+// Row (within the 32-row tile) held by accumulator register r of this lane.
+__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
 // Store this wave's accumulator tile into part[32][kPad] (fp32).
 __device__ __forceinline__ void store_tile(float* part, const f32x16& acc, int lane)
 {
-    const int col = lane & 31;
-    const int row0 = 4 * (lane >> 5);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        part[(8 * (r >> 2) + row0 + (r & 3)) * kPad + col] = acc[r];
+    for (int r = 0; r < 16; ++r) part[acc_row(r, lane) * kPad + (lane & 31)] = acc[r];
+}
+
+// The folded mixer of a tile: for the nb blocks whose x-rows (B per block,
+// 32 channels, fp32, row stride kPad) sit in xs, u[b] = sum_j mixl[b, j] * x[j]
+// for the slots b = 1 .. B-1 read out, with mixs the [B*B][32] bf16 slice of
+// mixl.  A thread takes one (slot, channel) and CH blocks at a time as
+// independent accumulation chains.
+template <int CH>
+__device__ __forceinline__ void mix_chains(const float* xs, const uint16_t* mixs, uint32_t nb,
+                                           uint32_t B, uint32_t n0, uint32_t c0, uint32_t R,
+                                           float* u_out, uint16_t* ub_out, int tid)
+{
+    const uint32_t bm1 = B - 1;
+    for (uint32_t t = tid; t < bm1 * kTile; t += kThreads) {
+        const uint32_t c = t & 31, b = 1 + (t >> 5);
+        const uint16_t* mrow = mixs + (size_t)b * B * kTile + c;
+        for (uint32_t lb0 = 0; lb0 < nb; lb0 += CH) {
+            const float* xq[CH];
+#pragma unroll
+            for (int q = 0; q < CH; ++q) {
+                const uint32_t lb = lb0 + q < nb ? lb0 + q : nb - 1;
+                xq[q] = xs + lb * B * kPad + c;
+            }
+            float acc[CH];
+#pragma unroll
+            for (int q = 0; q < CH; ++q) acc[q] = 0.0f;
+#pragma unroll 4
+            for (uint32_t j = 0; j < B; ++j) {
+                const float mv = from_bf16(mrow[j * kTile]);
+#pragma unroll
+                for (int q = 0; q < CH; ++q) acc[q] = fmaf(mv, xq[q][j * kPad], acc[q]);
+            }
+#pragma unroll
+            for (int q = 0; q < CH; ++q) {
+                if (lb0 + q < nb) {
+                    const size_t idx = ((size_t)(n0 + lb0 + q) * bm1 + (b - 1)) * R + c0 + c;
+                    u_out[idx] = acc[q];
+                    ub_out[idx] = to_bf16(acc[q]);
+                }
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void mix_tile(const float* xs, const uint16_t* mixs, uint32_t nb,
+                                         uint32_t B, uint32_t n0, uint32_t c0, uint32_t R,
+                                         float* u_out, uint16_t* ub_out, int tid)
+{
+    if (nb >= 4) {
+        mix_chains<8>(xs, mixs, nb, B, n0, c0, R, u_out, ub_out, tid);
+    } else {
+        mix_chains<1>(xs, mixs, nb, B, n0, c0, R, u_out, ub_out, tid);
     }
 }
 
@@ -126,16 +217,22 @@ struct MixArgs {
     uint32_t N, B, R, bpt, col_tiles;
 };
 
-// One workgroup per (tile of bpt whole blocks = bpt * B x-rows, 32 channels).
+// One workgroup per (bpt whole blocks -- at most 32 * WR x-rows -- and 32
+// channels).  Wave w takes the 32-row slab w % WR and the K range w / WR of
+// WK equal parts.
+template <int WR, int WK>
 __global__ void __launch_bounds__(kThreads) latent_mix_kernel(MixArgs a)
 {
-    __shared__ float part[kWaves][kTile * kPad];
-    __shared__ uint16_t xhs[kTile * kTile];
+    static_assert(WR * WK == kWaves, "four waves");
+    constexpr int kRows = WR * kTile;
+    __shared__ float part[WK][kRows * kPad];
+    __shared__ uint16_t xhs[kRows * kTile];
     extern __shared__ u32x4 mixs_dyn[];  // [B * B][32] bf16 slice of mixl
     const uint16_t* mixs = reinterpret_cast<const uint16_t*>(mixs_dyn);
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, half = lane >> 5;
+    const int wr = wave % WR, wk = wave / WR;
     const uint32_t ct = blockIdx.x % a.col_tiles;
     const uint32_t rt = blockIdx.x / a.col_tiles;
     const uint32_t c0 = ct * kTile;
@@ -147,61 +244,47 @@ __global__ void __launch_bounds__(kThreads) latent_mix_kernel(MixArgs a)
     // the mixer slice [B*B rows of 32 channels] and the cache tile to LDS
     const uint32_t mix_chunks = B * B * 4;  // 16-byte chunks
     for (uint32_t q = tid; q < mix_chunks; q += kThreads) {
-        const uint32_t row = q >> 2, part16 = q & 3;
-        mixs_dyn[q] = *reinterpret_cast<const u32x4*>(a.mixl + (size_t)row * R + c0 + 8 * part16);
+        mixs_dyn[q] = load16(a.mixl + (size_t)(q >> 2) * R + c0 + 8 * (q & 3));
     }
-    if (tid < kTile * 4) {
-        const uint32_t i = tid >> 2, part16 = tid & 3;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (i < rows) {
-            v = *reinterpret_cast<const u32x4*>(a.xh + ((size_t)n0 * B + i) * R + c0 + 8 * part16);
-        }
-        *reinterpret_cast<u32x4*>(xhs + i * kTile + 8 * part16) = v;
+    for (uint32_t q = tid; q < (uint32_t)kRows * 4; q += kThreads) {
+        const uint32_t i = q >> 2, p = q & 3;
+        const uint32_t ic = i < rows ? i : 0;
+        const u32x4 v = load16(a.xh + ((size_t)n0 * B + ic) * R + c0 + 8 * p);
+        *reinterpret_cast<u32x4*>(xhs + i * kTile + 8 * p) = v & (i < rows ? ~0u : 0u);
     }
 
-    // x-row this lane supplies to A: the embedding of the previous token
-    const uint32_t i = lane & 31;
-    const uint16_t* a_row = nullptr;
-    if (i < rows) {
-        const uint32_t lb = i / B, slot = i % B;
-        const uint32_t n = n0 + lb;
-        const int64_t tok = (slot == 0) ? a.am1[n] : a.blk[(size_t)n * B + slot - 1];
-        // an id outside [0, V) reads as a zero embedding row
-        if (tok >= 0 && tok < a.V) a_row = a.w1 + (size_t)tok * R;
-    }
-    const uint16_t* b_row = a.wlat + (size_t)(c0 + i) * R;
-    const int k_len = (int)(R / kWaves);
-    f32x16 acc = {};
-    mfma_range(acc, a_row, b_row, wave * k_len, k_len, half);
-    store_tile(part[wave], acc, lane);
+    // A row of this lane: the embedding of the previous slot's token
+    const uint32_t i = wr * kTile + (lane & 31);
+    const uint32_t ic = i < rows ? i : 0;
+    const uint32_t n = n0 + ic / B, slot = ic % B;
+    const int64_t tok = (slot == 0) ? a.am1[n] : a.blk[(size_t)n * B + slot - 1];
+    // an id outside [0, V) (and a padding row) reads as a zero embedding row
+    const bool tok_ok = i < rows && tok >= 0 && tok < a.V;
+    const uint16_t* ap = a.w1 + (size_t)(tok_ok ? tok : 0) * R + 8 * half;
+    const uint16_t* bp[1] = {a.wlat + (size_t)(c0 + (lane & 31)) * R + 8 * half};
+    const int steps = (int)(R / 16) / WK;
+    f32x16 acc[1] = {};
+    mma_k<1>(acc, ap, bp, wk * steps * 16, steps, tok_ok ? ~0u : 0u);
+    store_tile(&part[wk][wr * kTile * kPad], acc[0], lane);
     __syncthreads();
 
-    // x = cache + sum of the 4 K-partials, kept in part[0]
-    for (int e = tid; e < kTile * kTile; e += kThreads) {
+    // x = cache + the K-partials, kept in part[0]
+    for (int e = tid; e < kRows * kTile; e += kThreads) {
         const int r = e >> 5, c = e & 31;
         const int o = r * kPad + c;
-        const float x = ((part[0][o] + part[1][o]) + (part[2][o] + part[3][o])) +
-                        from_bf16(xhs[r * kTile + c]);
-        part[0][o] = x;
+        float x;
+        if constexpr (WK == 4) {
+            x = (part[0][o] + part[1][o]) + (part[2][o] + part[3][o]);
+        } else if constexpr (WK == 2) {
+            x = part[0][o] + part[1][o];
+        } else {
+            x = part[0][o];
+        }
+        part[0][o] = x + from_bf16(xhs[r * kTile + c]);
     }
     __syncthreads();
 
-    // folded mixer for the slots read out: u[b] = sum_j mixl[b, j] * x[j]
-    const uint32_t bm1 = B - 1;
-    const uint32_t outs = nb * bm1 * kTile;
-    for (uint32_t e = tid; e < outs; e += kThreads) {
-        const uint32_t c = e & 31, q = e >> 5;
-        const uint32_t lb = q / bm1, b = 1 + q % bm1;
-        const float* xcol = &part[0][lb * B * kPad + c];
-        const uint16_t* mrow = mixs + (size_t)b * B * kTile + c;
-        float u = 0.0f;
-        for (uint32_t j = 0; j < B; ++j) {
-            u = fmaf(from_bf16(mrow[j * kTile]), xcol[j * kPad], u);
-        }
-        const size_t row_out = (size_t)(n0 + lb) * bm1 + (b - 1);
-        a.u[row_out * R + c0 + c] = u;
-        a.ub[row_out * R + c0 + c] = to_bf16(u);
-    }
+    mix_tile(&part[0][0], mixs, nb, B, n0, c0, R, a.u, a.ub, tid);
 }
 
 struct GateArgs {
@@ -212,32 +295,58 @@ struct GateArgs {
     uint32_t rows, R, H, col_tiles;
 };
 
-// One workgroup per (32 rows, 32 hidden units).
+// g * sigmoid(g) * v in fp32: the accurate exp, then the hardware reciprocal
+// (about 1 ulp) instead of a correctly rounded division.
+__device__ __forceinline__ float swiglu(float g, float v)
+{
+    return g * __builtin_amdgcn_rcpf(1.0f + expf(-g)) * v;
+}
+
+// One workgroup per (32 * WR rows, 32 hidden units); g and v share A.
+template <int WR, int WK>
 __global__ void __launch_bounds__(kThreads) latent_gate_kernel(GateArgs a)
 {
-    __shared__ float part[2][kWaves][kTile * kPad];
+    static_assert(WR * WK == kWaves, "four waves");
+    constexpr int kRows = WR * kTile;
+    __shared__ float part[2][WK > 1 ? WK : 1][WK > 1 ? kRows * kPad : 1];
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, half = lane >> 5;
+    const int wr = wave % WR, wk = wave / WR;
     const uint32_t ht = blockIdx.x % a.col_tiles;
     const uint32_t rt = blockIdx.x / a.col_tiles;
-    const uint32_t h0 = ht * kTile, i0 = rt * kTile;
-    const uint32_t i = lane & 31;
-    const uint16_t* a_row = (i0 + i < a.rows) ? a.ub + (size_t)(i0 + i) * a.R : nullptr;
-    const int k_len = (int)(a.R / kWaves);
-    f32x16 g = {}, v = {};
-    mfma_range(g, a_row, a.wg + (size_t)(h0 + i) * a.R, wave * k_len, k_len, half);
-    mfma_range(v, a_row, a.wu + (size_t)(h0 + i) * a.R, wave * k_len, k_len, half);
-    store_tile(part[0][wave], g, lane);
-    store_tile(part[1][wave], v, lane);
-    __syncthreads();
-    for (int e = tid; e < kTile * kTile; e += kThreads) {
-        const int r = e >> 5, c = e & 31;
-        if (i0 + r >= a.rows) continue;
-        const int o = r * kPad + c;
-        const float gs = (part[0][0][o] + part[0][1][o]) + (part[0][2][o] + part[0][3][o]);
-        const float vs = (part[1][0][o] + part[1][1][o]) + (part[1][2][o] + part[1][3][o]);
-        const float f = gs / (1.0f + expf(-gs)) * vs;
-        a.m[(size_t)(i0 + r) * a.H + h0 + c] = to_bf16(f);
+    const uint32_t h0 = ht * kTile, i0 = rt * kRows;
+    const uint32_t row = i0 + wr * kTile + (lane & 31);
+    const uint32_t rowc = row < a.rows ? row : a.rows - 1;  // padding rows: any valid row
+    const uint16_t* ap = a.ub + (size_t)rowc * a.R + 8 * half;
+    const uint16_t* bp[2] = {a.wg + (size_t)(h0 + (lane & 31)) * a.R + 8 * half,
+                             a.wu + (size_t)(h0 + (lane & 31)) * a.R + 8 * half};
+    const int steps = (int)(a.R / 16) / WK;
+    f32x16 acc[2] = {};
+    mma_k<2>(acc, ap, bp, wk * steps * 16, steps, ~0u);
+    if constexpr (WK == 1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const uint32_t rr = i0 + wr * kTile + acc_row(r, lane);
+            if (rr < a.rows) a.m[(size_t)rr * a.H + h0 + (lane & 31)] = to_bf16(swiglu(acc[0][r], acc[1][r]));
+        }
+    } else {
+        store_tile(&part[0][wk][wr * kTile * kPad], acc[0], lane);
+        store_tile(&part[1][wk][wr * kTile * kPad], acc[1], lane);
+        __syncthreads();
+        for (int e = tid; e < kRows * kTile; e += kThreads) {
+            const int r = e >> 5, c = e & 31;
+            if (i0 + r >= a.rows) continue;
+            const int o = r * kPad + c;
+            float gs, vs;
+            if constexpr (WK == 4) {
+                gs = (part[0][0][o] + part[0][1][o]) + (part[0][2][o] + part[0][3][o]);
+                vs = (part[1][0][o] + part[1][1][o]) + (part[1][2][o] + part[1][3][o]);
+            } else {
+                gs = part[0][0][o] + part[0][1][o];
+                vs = part[1][0][o] + part[1][1][o];
+            }
+            a.m[(size_t)(i0 + r) * a.H + h0 + c] = to_bf16(swiglu(gs, vs));
+        }
     }
 }
 
@@ -249,30 +358,376 @@ struct DownArgs {
     uint32_t rows, R, H, col_tiles;
 };
 
-// One workgroup per (32 rows, 32 channels).
+// One workgroup per (32 * WR rows, 32 channels).
+template <int WR, int WK>
 __global__ void __launch_bounds__(kThreads) latent_down_kernel(DownArgs a)
 {
-    __shared__ float part[kWaves][kTile * kPad];
+    static_assert(WR * WK == kWaves, "four waves");
+    constexpr int kRows = WR * kTile;
+    __shared__ float part[WK > 1 ? WK : 1][WK > 1 ? kRows * kPad : 1];
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, half = lane >> 5;
+    const int wr = wave % WR, wk = wave / WR;
     const uint32_t ct = blockIdx.x % a.col_tiles;
     const uint32_t rt = blockIdx.x / a.col_tiles;
-    const uint32_t c0 = ct * kTile, i0 = rt * kTile;
-    const uint32_t i = lane & 31;
-    const uint16_t* a_row = (i0 + i < a.rows) ? a.m + (size_t)(i0 + i) * a.H : nullptr;
-    const int k_len = (int)(a.H / kWaves);
-    f32x16 acc = {};
-    mfma_range(acc, a_row, a.wd + (size_t)(c0 + i) * a.H, wave * k_len, k_len, half);
-    store_tile(part[wave], acc, lane);
-    __syncthreads();
-    for (int e = tid; e < kTile * kTile; e += kThreads) {
-        const int r = e >> 5, c = e & 31;
-        if (i0 + r >= a.rows) continue;
-        const int o = r * kPad + c;
-        const size_t idx = (size_t)(i0 + r) * a.R + c0 + c;
-        const float mm = (part[0][o] + part[1][o]) + (part[2][o] + part[3][o]);
-        a.out[idx] = to_bf16(a.u[idx] + mm);
+    const uint32_t c0 = ct * kTile, i0 = rt * kRows;
+    const uint32_t row = i0 + wr * kTile + (lane & 31);
+    const uint32_t rowc = row < a.rows ? row : a.rows - 1;
+    const uint16_t* ap = a.m + (size_t)rowc * a.H + 8 * half;
+    const uint16_t* bp[1] = {a.wd + (size_t)(c0 + (lane & 31)) * a.H + 8 * half};
+    const int steps = (int)(a.H / 16) / WK;
+    if constexpr (WK == 1) {
+        // the residual, fetched ahead of the products
+        float res[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const uint32_t rr = i0 + wr * kTile + acc_row(r, lane);
+            res[r] = a.u[(size_t)(rr < a.rows ? rr : a.rows - 1) * a.R + c0 + (lane & 31)];
+        }
+        f32x16 acc[1] = {};
+        mma_k<1>(acc, ap, bp, 0, steps, ~0u);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const uint32_t rr = i0 + wr * kTile + acc_row(r, lane);
+            if (rr < a.rows) a.out[(size_t)rr * a.R + c0 + (lane & 31)] = to_bf16(res[r] + acc[0][r]);
+        }
+    } else {
+        constexpr int kPer = kRows * kTile / kThreads;  // elements per thread
+        float res[kPer];
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const int e = tid + q * kThreads;
+            const uint32_t rr = i0 + (e >> 5);
+            res[q] = a.u[(size_t)(rr < a.rows ? rr : a.rows - 1) * a.R + c0 + (e & 31)];
+        }
+        f32x16 acc[1] = {};
+        mma_k<1>(acc, ap, bp, wk * steps * 16, steps, ~0u);
+        store_tile(&part[wk][wr * kTile * kPad], acc[0], lane);
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const int e = tid + q * kThreads;
+            const int r = e >> 5, c = e & 31;
+            if (i0 + r >= a.rows) continue;
+            const int o = r * kPad + c;
+            float mm;
+            if constexpr (WK == 4) {
+                mm = (part[0][o] + part[1][o]) + (part[2][o] + part[3][o]);
+            } else {
+                mm = part[0][o] + part[1][o];
+            }
+            a.out[(size_t)(i0 + r) * a.R + c0 + c] = to_bf16(res[q] + mm);
+        }
     }
+}
+
+// ---------------------------------------------------------------------------
+// LDS-staged variants for many rows.  A workgroup computes 128 rows (one
+// 32-row slab per wave) of one or more 32-column tiles.  The contraction is
+// walked in chunks of 64; the A and B rows of a chunk are copied straight
+// from global memory into LDS by the 16-byte load-to-LDS instruction (eight
+// lanes per 128-byte row segment, so every load instruction reads eight whole
+// cache lines), four chunks in flight at once, and the matrix cores read
+// their operands back with 16-byte LDS loads.  Within an LDS row the 16-byte
+// columns are permuted by XOR with (row & 7) so that the 32 rows an operand
+// load touches spread over the LDS banks.
+// ---------------------------------------------------------------------------
+constexpr int kKC = 64;           // contraction elements per chunk
+constexpr int kRing = 4;          // chunks in flight
+constexpr int kSlabRows = 128;    // A rows of a staged workgroup
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Rows [32 j + 8 w, +8) of a chunk are loaded by wave w's j-th instruction;
+// lane l reads row 32 j + 8 w + l / 8, logical 16-byte column (l % 8) ^ (l / 8),
+// and lands in LDS at row-major position (row, l % 8).
+template <int ROWS>
+struct DmaRows {
+    static constexpr int kN = ROWS / 32;  // load instructions per wave per chunk
+    const uint16_t* src[kN];              // this lane's row, at its swizzled column
+};
+
+// One 16-byte load-to-LDS: lane l's 16 bytes from gsrc land at LDS byte
+// address lds_base + 16 l (lds_base wave-uniform, carried in M0).  Issued as
+// the two instructions the compiler itself emits for this load, so that its
+// wait-count pass does not add a wait for every pending load before each LDS
+// read; the contraction loop waits for exactly the chunk it is about to read
+// (wait_vmcnt), and extra loads the compiler places after these only make
+// its own waits stricter.
+__device__ __forceinline__ void dma16(const uint16_t* gsrc, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gsrc), "s"(lds_base)
+                 : "memory", "m0");
+}
+
+// LDS byte address of a __shared__ element, made wave-uniform.
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p)
+{
+    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
+    return __builtin_amdgcn_readfirstlane(a);
+}
+
+template <int ROWS>
+__device__ __forceinline__ void dma_chunk(const DmaRows<ROWS>& d, uint16_t* lds_slot, int k0,
+                                          int wave)
+{
+#pragma unroll
+    for (int j = 0; j < DmaRows<ROWS>::kN; ++j) {
+        dma16(d.src[j] + k0, lds_addr(lds_slot + (32 * j + 8 * wave) * kKC));
+    }
+}
+
+// MFMA operand: logical row r, k = 16 s + 8 (lane / 32) of a staged chunk.
+__device__ __forceinline__ bf16x8 lds_operand(const uint16_t* lds_slot, int r0, int s, int lane)
+{
+    const int r = r0 + (lane & 31);
+    const int q = (2 * s + (lane >> 5)) ^ (r & 7);
+    return __builtin_bit_cast(bf16x8,
+                              *reinterpret_cast<const u32x4*>(lds_slot + r * kKC + 8 * q));
+}
+
+template <int ROWS>
+__device__ __forceinline__ void dma_setup(DmaRows<ROWS>& d, const uint16_t* const* row_base,
+                                          int lane)
+{
+#pragma unroll
+    for (int j = 0; j < DmaRows<ROWS>::kN; ++j) {
+        d.src[j] = row_base[j] + 8 * ((lane & 7) ^ (lane >> 3));
+    }
+}
+
+// Wait until this wave's loads of chunk c have landed, given `ahead` later
+// chunks already issued (0 .. kRing-1), each PER load instructions.
+template <int PER>
+__device__ __forceinline__ void wait_chunk(int ahead)
+{
+    switch (ahead) {
+        case 3: wait_vmcnt<3 * PER>(); break;
+        case 2: wait_vmcnt<2 * PER>(); break;
+        case 1: wait_vmcnt<1 * PER>(); break;
+        default: wait_vmcnt<0>(); break;
+    }
+}
+
+// acc[t] += A[wave slab] * B[tile t] over the contraction (nc chunks).
+// zero_row: bit q set when A row (lane / 8) + 8 * wave + 32 q must read as
+// zeros (an invalid embedding id); those LDS rows are cleared after landing.
+template <int ROWS_A, int ROWS_B, int NT>
+__device__ __forceinline__ void staged_mma(f32x16 (&acc)[NT], const DmaRows<ROWS_A>& da,
+                                           const DmaRows<ROWS_B>& db,
+                                           uint16_t (*lds_a)[ROWS_A * kKC],
+                                           uint16_t (*lds_b)[ROWS_B * kKC], int nc, int tid,
+                                           uint32_t zero_row)
+{
+    constexpr int kPer = DmaRows<ROWS_A>::kN + DmaRows<ROWS_B>::kN;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int first = nc < kRing ? nc : kRing;
+    for (int c = 0; c < first; ++c) {
+        dma_chunk(da, lds_a[c], c * kKC, wave);
+        dma_chunk(db, lds_b[c], c * kKC, wave);
+    }
+    for (int c = 0; c < nc; ++c) {
+        const int slot = c % kRing;
+        const int issued = (c + kRing < nc ? c + kRing : nc);  // chunks issued so far
+        wait_chunk<kPer>(issued - 1 - c);
+        if (zero_row) {
+#pragma unroll
+            for (int q = 0; q < DmaRows<ROWS_A>::kN; ++q) {
+                if (zero_row & (1u << q)) {
+                    *reinterpret_cast<u32x4*>(lds_a[slot] + (32 * q + 8 * wave + (lane >> 3)) * kKC +
+                                              8 * (lane & 7)) = u32x4{0u, 0u, 0u, 0u};
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < kKC / 16; ++s) {
+            const bf16x8 av = lds_operand(lds_a[slot], kTile * wave, s, lane);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    av, lds_operand(lds_b[slot], kTile * t, s, lane), acc[t], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+        if (c + kRing < nc) {
+            dma_chunk(da, lds_a[slot], (c + kRing) * kKC, wave);
+            dma_chunk(db, lds_b[slot], (c + kRing) * kKC, wave);
+        }
+    }
+}
+
+// gate, staged: 128 rows x 32*NH hidden units; B holds NH tiles of wg, then
+// the NH matching tiles of wu.
+template <int NH>
+__global__ void __launch_bounds__(kThreads) latent_gate_staged(GateArgs a)
+{
+    constexpr int kB = 2 * kTile * NH;
+    __shared__ __attribute__((aligned(16))) uint16_t lds_a[kRing][kSlabRows * kKC];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_b[kRing][kB * kKC];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const uint32_t col_tiles = a.H / (kTile * NH);
+    const uint32_t ht = blockIdx.x % col_tiles;
+    const uint32_t rt = blockIdx.x / col_tiles;
+    const uint32_t h0 = ht * kTile * NH, i0 = rt * kSlabRows;
+    const uint16_t* abase[DmaRows<kSlabRows>::kN];
+#pragma unroll
+    for (int j = 0; j < DmaRows<kSlabRows>::kN; ++j) {
+        const uint32_t row = i0 + 32 * j + 8 * wave + (lane >> 3);
+        abase[j] = a.ub + (size_t)(row < a.rows ? row : 0) * a.R;  // padding rows: any row
+    }
+    const uint16_t* bbase[DmaRows<kB>::kN];
+#pragma unroll
+    for (int j = 0; j < DmaRows<kB>::kN; ++j) {
+        const uint32_t br = 32 * j + 8 * wave + (lane >> 3);
+        const uint32_t hr = h0 + br % (kTile * NH);
+        bbase[j] = (br < (uint32_t)(kTile * NH) ? a.wg : a.wu) + (size_t)hr * a.R;
+    }
+    DmaRows<kSlabRows> da;
+    DmaRows<kB> db;
+    dma_setup(da, abase, lane);
+    dma_setup(db, bbase, lane);
+    f32x16 acc[2 * NH] = {};
+    staged_mma<kSlabRows, kB, 2 * NH>(acc, da, db, lds_a, lds_b, (int)(a.R / kKC), tid, 0u);
+#pragma unroll
+    for (int t = 0; t < NH; ++t) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const uint32_t rr = i0 + kTile * wave + acc_row(r, lane);
+            if (rr < a.rows) {
+                a.m[(size_t)rr * a.H + h0 + kTile * t + (lane & 31)] =
+                    to_bf16(swiglu(acc[t][r], acc[NH + t][r]));
+            }
+        }
+    }
+}
+
+// down, staged: 128 rows x 32 channels, plus the residual.
+__global__ void __launch_bounds__(kThreads) latent_down_staged(DownArgs a)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t lds_a[kRing][kSlabRows * kKC];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_b[kRing][kTile * kKC];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const uint32_t ct = blockIdx.x % a.col_tiles;
+    const uint32_t rt = blockIdx.x / a.col_tiles;
+    const uint32_t c0 = ct * kTile, i0 = rt * kSlabRows;
+    // the residual first: these loads are older than the chunk loads the
+    // contraction counts
+    float res[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const uint32_t rr = i0 + kTile * wave + acc_row(r, lane);
+        res[r] = a.u[(size_t)(rr < a.rows ? rr : 0) * a.R + c0 + (lane & 31)];
+    }
+    const uint16_t* abase[DmaRows<kSlabRows>::kN];
+#pragma unroll
+    for (int j = 0; j < DmaRows<kSlabRows>::kN; ++j) {
+        const uint32_t row = i0 + 32 * j + 8 * wave + (lane >> 3);
+        abase[j] = a.m + (size_t)(row < a.rows ? row : 0) * a.H;
+    }
+    const uint16_t* bbase[1] = {a.wd + (size_t)(c0 + 8 * wave + (lane >> 3)) * a.H};
+    DmaRows<kSlabRows> da;
+    DmaRows<kTile> db;
+    dma_setup(da, abase, lane);
+    dma_setup(db, bbase, lane);
+    f32x16 acc[1] = {};
+    staged_mma<kSlabRows, kTile, 1>(acc, da, db, lds_a, lds_b, (int)(a.H / kKC), tid, 0u);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const uint32_t rr = i0 + kTile * wave + acc_row(r, lane);
+        if (rr < a.rows) a.out[(size_t)rr * a.R + c0 + (lane & 31)] = to_bf16(res[r] + acc[0][r]);
+    }
+}
+
+// mix, staged: bpt = 128 / B whole blocks (their x-rows gathered from w1)
+// x 32 channels, then the folded mixer from LDS.
+__global__ void __launch_bounds__(kThreads) latent_mix_staged(MixArgs a)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t lds_a[kRing][kSlabRows * kKC];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_b[kRing][kTile * kKC];
+    extern __shared__ u32x4 mixs_dyn[];  // [B * B][32] bf16 slice of mixl
+    const uint16_t* mixs = reinterpret_cast<const uint16_t*>(mixs_dyn);
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const uint32_t ct = blockIdx.x % a.col_tiles;
+    const uint32_t rt = blockIdx.x / a.col_tiles;
+    const uint32_t c0 = ct * kTile;
+    const uint32_t B = a.B, R = a.R;
+    const uint32_t n0 = rt * a.bpt;
+    const uint32_t nb = (a.N - n0 < a.bpt) ? (a.N - n0) : a.bpt;
+    const uint32_t rows = nb * B;
+
+    // every load here is older than the chunk loads the contraction counts
+    const uint32_t mix_chunks = B * B * 4;
+    for (uint32_t q = tid; q < mix_chunks; q += kThreads) {
+        mixs_dyn[q] = load16(a.mixl + (size_t)(q >> 2) * R + c0 + 8 * (q & 3));
+    }
+    float xh[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const uint32_t i = kTile * wave + acc_row(r, lane);
+        xh[r] = from_bf16(a.xh[((size_t)n0 * B + (i < rows ? i : 0)) * R + c0 + (lane & 31)]);
+    }
+    const uint16_t* abase[DmaRows<kSlabRows>::kN];
+    uint32_t zero_row = 0;
+#pragma unroll
+    for (int j = 0; j < DmaRows<kSlabRows>::kN; ++j) {
+        const uint32_t i = 32 * j + 8 * wave + (lane >> 3);
+        const uint32_t ic = i < rows ? i : 0;
+        const uint32_t n = n0 + ic / B, slot = ic % B;
+        const int64_t tok = (slot == 0) ? a.am1[n] : a.blk[(size_t)n * B + slot - 1];
+        const bool ok = tok >= 0 && tok < a.V;
+        abase[j] = a.w1 + (size_t)(ok ? tok : 0) * R;
+        // an id outside [0, V) reads as a zero embedding row (padding rows
+        // beyond the tile's blocks are never read back)
+        if (i < rows && !ok) zero_row |= 1u << j;
+    }
+    const uint16_t* bbase[1] = {a.wlat + (size_t)(c0 + 8 * wave + (lane >> 3)) * R};
+    DmaRows<kSlabRows> da;
+    DmaRows<kTile> db;
+    dma_setup(da, abase, lane);
+    dma_setup(db, bbase, lane);
+    f32x16 acc[1] = {};
+    staged_mma<kSlabRows, kTile, 1>(acc, da, db, lds_a, lds_b, (int)(R / kKC), tid, zero_row);
+    // x = cache + projection, into LDS over the A staging area (free after
+    // the contraction's last barrier)
+    static_assert(kSlabRows * kPad * sizeof(float) <= sizeof(lds_a), "x tile fits the ring");
+    float* xs = reinterpret_cast<float*>(&lds_a[0][0]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        xs[(kTile * wave + acc_row(r, lane)) * kPad + (lane & 31)] = acc[0][r] + xh[r];
+    }
+    __syncthreads();
+    mix_tile(xs, mixs, nb, B, n0, c0, R, a.u, a.ub, tid);
+}
+
+// Workgroup shape per kernel: 1, 2 or 4 row slabs of the direct kernels, 8
+// for the LDS-staged kernel, 0 = chosen from the shape.
+constexpr int kStaged = 8;
+constexpr uint64_t kStagedFromRows = 2048;  // measured: direct wins at 1024 rows
+struct LatentTiles {
+    int mix = 0, gate = 0, down = 0;
+};
+std::mutex g_tiles_mu;
+LatentTiles g_tiles;
+
+// The largest slab count that still gives every compute unit a workgroup.
+int auto_slabs(uint64_t wgs_at_one_slab, int cus)
+{
+    if (wgs_at_one_slab >= 4ull * (uint64_t)cus) return 4;
+    if (wgs_at_one_slab >= 2ull * (uint64_t)cus) return 2;
+    return 1;
 }
 
 // Workspace carve-up: u (fp32), bf16(u) and m, each 256-byte aligned.
@@ -355,6 +810,23 @@ int xpress_latent_pass(const int64_t* blk, const int64_t* am1, const uint16_t* x
     uint16_t* ub = reinterpret_cast<uint16_t*>(base + s.ub_off);
     uint16_t* m = reinterpret_cast<uint16_t*>(base + s.m_off);
 
+    int cus = device_cus();
+    if (cus < 1) cus = 256;
+    LatentTiles t;
+    {
+        std::lock_guard<std::mutex> lk(g_tiles_mu);
+        t = g_tiles;
+    }
+
+    // mix: bpt = (32 * WR) / B whole blocks per workgroup (128 / B staged)
+    const uint64_t ctiles = (uint64_t)(R / kTile);
+    const uint64_t xrows = (uint64_t)N * B;  // staged from kStagedFromRows x-rows
+    int wr_mix = t.mix;
+    if (!wr_mix) {
+        wr_mix = xrows >= kStagedFromRows
+                     ? kStaged
+                     : auto_slabs((uint64_t)((N + kTile / B - 1) / (kTile / B)) * ctiles, cus);
+    }
     MixArgs ma;
     ma.blk = blk;
     ma.am1 = am1;
@@ -368,26 +840,56 @@ int xpress_latent_pass(const int64_t* blk, const int64_t* am1, const uint16_t* x
     ma.N = (uint32_t)N;
     ma.B = (uint32_t)B;
     ma.R = (uint32_t)R;
-    ma.bpt = (uint32_t)(kTile / B);
-    ma.col_tiles = (uint32_t)(R / kTile);
-    const uint64_t mix_tiles = (uint64_t)((N + ma.bpt - 1) / ma.bpt) * ma.col_tiles;
-    const uint64_t row_tiles = (uint64_t)((rows + kTile - 1) / kTile);
-    const uint64_t gate_wgs = row_tiles * (uint64_t)(H / kTile);
-    const uint64_t down_wgs = row_tiles * (uint64_t)(R / kTile);
-    if (mix_tiles > 0x7FFFFFFFull || gate_wgs > 0x7FFFFFFFull || down_wgs > 0x7FFFFFFFull) {
+    ma.bpt = (uint32_t)((wr_mix == kStaged ? kSlabRows : kTile * wr_mix) / B);
+    ma.col_tiles = (uint32_t)ctiles;
+    const uint64_t mix_wgs = (uint64_t)((N + ma.bpt - 1) / ma.bpt) * ctiles;
+
+    const uint64_t rows_u = (uint64_t)rows;
+    int wr_gate = t.gate, wr_down = t.down;
+    if (!wr_gate) {
+        wr_gate = rows_u >= kStagedFromRows ? kStaged
+                                            : auto_slabs((rows_u + kTile - 1) / kTile * (H / kTile), cus);
+    }
+    if (!wr_down) {
+        wr_down = rows_u >= kStagedFromRows ? kStaged
+                                            : auto_slabs((rows_u + kTile - 1) / kTile * ctiles, cus);
+    }
+    // staged gate: two hidden tiles per workgroup when that still fills the chip
+    const uint64_t slabs128 = (rows_u + kSlabRows - 1) / kSlabRows;
+    const int gate_nh = (H % 64 == 0 && slabs128 * (uint64_t)(H / 64) >= (uint64_t)cus) ? 2 : 1;
+    const uint64_t gate_wgs = wr_gate == kStaged
+                                  ? slabs128 * (uint64_t)(H / (kTile * gate_nh))
+                                  : (rows_u + kTile * wr_gate - 1) / (kTile * wr_gate) * (H / kTile);
+    const uint64_t down_wgs = wr_down == kStaged
+                                  ? slabs128 * ctiles
+                                  : (rows_u + kTile * wr_down - 1) / (kTile * wr_down) * ctiles;
+    if (mix_wgs > 0x7FFFFFFFull || gate_wgs > 0x7FFFFFFFull || down_wgs > 0x7FFFFFFFull) {
         return XPRESS_EINVAL;
     }
+
     const size_t mix_lds = (size_t)B * B * kTile * 2u;
-    if (mix_lds > 32768u) {
+    const void* mix_fn = wr_mix == kStaged ? reinterpret_cast<const void*>(&latent_mix_staged)
+                       : wr_mix == 4 ? reinterpret_cast<const void*>(&latent_mix_kernel<4, 1>)
+                       : wr_mix == 2 ? reinterpret_cast<const void*>(&latent_mix_kernel<2, 2>)
+                                     : reinterpret_cast<const void*>(&latent_mix_kernel<1, 4>);
+    if (mix_lds > 16384u) {
         // the mixer slice of a large block size takes most of the LDS (up to
-        // 64 KiB at B = 32, beside 18.5 KiB of static LDS)
-        hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(&latent_mix_kernel),
-                                            hipFuncAttributeMaxDynamicSharedMemorySize,
+        // 64 KiB at B = 32, beside at most 46 KiB of static LDS)
+        hipError_t ea = hipFuncSetAttribute(mix_fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                             (int)mix_lds);
         if (ea != hipSuccess) return hip_fail(ea);
     }
-    hipLaunchKernelGGL(latent_mix_kernel, dim3((uint32_t)mix_tiles), dim3(kThreads), mix_lds,
-                       stream, ma);
+    const dim3 blk3(kThreads);
+    const dim3 mix_grid((uint32_t)mix_wgs);
+    if (wr_mix == kStaged) {
+        hipLaunchKernelGGL(latent_mix_staged, mix_grid, blk3, mix_lds, stream, ma);
+    } else if (wr_mix == 4) {
+        hipLaunchKernelGGL((latent_mix_kernel<4, 1>), mix_grid, blk3, mix_lds, stream, ma);
+    } else if (wr_mix == 2) {
+        hipLaunchKernelGGL((latent_mix_kernel<2, 2>), mix_grid, blk3, mix_lds, stream, ma);
+    } else {
+        hipLaunchKernelGGL((latent_mix_kernel<1, 4>), mix_grid, blk3, mix_lds, stream, ma);
+    }
 
     GateArgs ga;
     ga.ub = ub;
@@ -398,8 +900,18 @@ int xpress_latent_pass(const int64_t* blk, const int64_t* am1, const uint16_t* x
     ga.R = (uint32_t)R;
     ga.H = (uint32_t)H;
     ga.col_tiles = (uint32_t)(H / kTile);
-    hipLaunchKernelGGL(latent_gate_kernel, dim3((uint32_t)gate_wgs), dim3(kThreads), 0, stream,
-                       ga);
+    const dim3 gate_grid((uint32_t)gate_wgs);
+    if (wr_gate == kStaged && gate_nh == 2) {
+        hipLaunchKernelGGL((latent_gate_staged<2>), gate_grid, blk3, 0, stream, ga);
+    } else if (wr_gate == kStaged) {
+        hipLaunchKernelGGL((latent_gate_staged<1>), gate_grid, blk3, 0, stream, ga);
+    } else if (wr_gate == 4) {
+        hipLaunchKernelGGL((latent_gate_kernel<4, 1>), gate_grid, blk3, 0, stream, ga);
+    } else if (wr_gate == 2) {
+        hipLaunchKernelGGL((latent_gate_kernel<2, 2>), gate_grid, blk3, 0, stream, ga);
+    } else {
+        hipLaunchKernelGGL((latent_gate_kernel<1, 4>), gate_grid, blk3, 0, stream, ga);
+    }
 
     DownArgs da;
     da.m = m;
@@ -409,11 +921,31 @@ int xpress_latent_pass(const int64_t* blk, const int64_t* am1, const uint16_t* x
     da.rows = (uint32_t)rows;
     da.R = (uint32_t)R;
     da.H = (uint32_t)H;
-    da.col_tiles = (uint32_t)(R / kTile);
-    hipLaunchKernelGGL(latent_down_kernel, dim3((uint32_t)down_wgs), dim3(kThreads), 0, stream,
-                       da);
+    da.col_tiles = (uint32_t)ctiles;
+    const dim3 down_grid((uint32_t)down_wgs);
+    if (wr_down == kStaged) {
+        hipLaunchKernelGGL(latent_down_staged, down_grid, blk3, 0, stream, da);
+    } else if (wr_down == 4) {
+        hipLaunchKernelGGL((latent_down_kernel<4, 1>), down_grid, blk3, 0, stream, da);
+    } else if (wr_down == 2) {
+        hipLaunchKernelGGL((latent_down_kernel<2, 2>), down_grid, blk3, 0, stream, da);
+    } else {
+        hipLaunchKernelGGL((latent_down_kernel<1, 4>), down_grid, blk3, 0, stream, da);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e);
+    return XPRESS_OK;
+}
+
+int xpress_latent_set_tiles(int mix, int gate, int down)
+{
+    for (int v : {mix, gate, down}) {
+        if (v != 0 && v != 1 && v != 2 && v != 4 && v != kStaged) return XPRESS_EINVAL;
+    }
+    std::lock_guard<std::mutex> lk(g_tiles_mu);
+    g_tiles.mix = mix;
+    g_tiles.gate = gate;
+    g_tiles.down = down;
     return XPRESS_OK;
 }
 

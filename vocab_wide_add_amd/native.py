@@ -64,6 +64,8 @@ def load():
         lib.xpress_readout_gemm_argmax_to_blk.restype = i32
         lib.xpress_latent_pass.argtypes = [vp] * 10 + [i64] * 5 + [vp]
         lib.xpress_latent_pass.restype = i32
+        lib.xpress_latent_set_tiles.argtypes = [i32, i32, i32]
+        lib.xpress_latent_set_tiles.restype = i32
         lib.xpress_latent_reserve.argtypes = [i64, i64, i64, i64, vp]
         lib.xpress_latent_reserve.restype = i32
         lib.xpress_reserve.argtypes = [i64, i64, i64, vp]
@@ -166,6 +168,12 @@ def xpress_latent_pass(blk, am1, xh, w1, wlat, mixl, wg, wu, wd, lat_out, N: int
 def xpress_latent_reserve(N: int, B: int, R: int, H: int, stream=None) -> None:
     _check(load().xpress_latent_reserve(int(N), int(B), int(R), int(H), _stream(stream)),
            "xpress_latent_reserve")
+
+
+def xpress_latent_set_tiles(mix: int = 0, gate: int = 0, down: int = 0) -> None:
+    """Row-slab counts (1, 2, 4; 0 = automatic) of the three latent kernels."""
+    _check(load().xpress_latent_set_tiles(int(mix), int(gate), int(down)),
+           "xpress_latent_set_tiles")
 
 
 def xpress_reserve(N: int, B: int, V: int, stream=None) -> None:
