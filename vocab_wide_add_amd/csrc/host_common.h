@@ -29,9 +29,12 @@ XPRESS_INTERNAL bool ranges_overlap(const void* p0, size_t n0, const void* p1, s
 XPRESS_INTERNAL int workspace_table(hipStream_t stream, int64_t entries, uint64_t** table);
 
 // Second pass of a split readout: for every row the largest of its `splits`
-// packed keys in table[row * splits ...] becomes blk[n, 1 + b].
-XPRESS_INTERNAL hipError_t launch_reduce_table(uint64_t* table, int64_t* blk, uint32_t rows,
-                                               uint32_t bm1, uint32_t splits,
+// packed keys in table[row * splits ...] names the winner, and blk[n, 1 + b]
+// receives its index, or cand[row * V + index] when cand is not null (the
+// top-C readout's candidate ids, V candidates per row).
+XPRESS_INTERNAL hipError_t launch_reduce_table(uint64_t* table, int64_t* blk,
+                                               const int64_t* cand, uint32_t rows,
+                                               uint32_t bm1, uint32_t V, uint32_t splits,
                                                hipStream_t stream);
 
 }  // namespace xpress

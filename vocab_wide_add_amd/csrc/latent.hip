@@ -456,17 +456,24 @@ struct DmaRows {
 
 // One 16-byte load-to-LDS: lane l's 16 bytes from gsrc land at LDS byte
 // address lds_base + 16 l (lds_base wave-uniform, carried in M0).  Issued as
-// the two instructions the compiler itself emits for this load, so that its
+// the instructions the compiler itself emits for this load, so that its
 // wait-count pass does not add a wait for every pending load before each LDS
 // read; the contraction loop waits for exactly the chunk it is about to read
 // (wait_vmcnt), and extra loads the compiler places after these only make
 // its own waits stricter.
 __device__ __forceinline__ void dma16(const uint16_t* gsrc, uint32_t lds_base)
 {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(gsrc), "s"(lds_base)
-                 : "memory", "m0");
+    // M0 is read when the load issues; it is restored right after so that no
+    // other use of M0 sees the LDS address
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(gsrc), "s"(lds_base)
+        : "memory");
 }
 
 // LDS byte address of a __shared__ element, made wave-uniform.

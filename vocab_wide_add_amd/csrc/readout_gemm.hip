@@ -335,7 +335,8 @@ extern "C" int xpress_readout_gemm_argmax_to_blk(const uint16_t* base, const uin
         default: e = launch_gemm<256>(a, grid, stream); break;
     }
     if (e != hipSuccess) return hip_fail(e);
-    e = launch_reduce_table(a.table, blk, a.rows, (uint32_t)(B - 1), a.ranges, stream);
+    e = launch_reduce_table(a.table, blk, nullptr, a.rows, (uint32_t)(B - 1), a.V, a.ranges,
+                            stream);
     if (e != hipSuccess) return hip_fail(e);
     return XPRESS_OK;
 }

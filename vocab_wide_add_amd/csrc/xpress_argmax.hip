@@ -370,19 +370,27 @@ __global__ __launch_bounds__(256) void topc_wave_kernel(const uint16_t* __restri
     }
 }
 
-// Second pass of the two-pass combine: one thread per row reduces the row's
-// `splits` keys (a larger key is a larger value or, on equal values, a
-// smaller index) and writes blk.
+// Second pass of the two-pass combine: one wave per row reads the row's
+// `splits` keys with consecutive lanes on consecutive keys, keeps the largest
+// (a larger key is a larger value or, on equal values, a smaller index),
+// reduces over the wave and writes blk from lane 0.
 __global__ __launch_bounds__(256) void reduce_keys_kernel(RowArgs a)
 {
-    for (uint32_t row = blockIdx.x * 256u + threadIdx.x; row < a.rows;
-         row += gridDim.x * 256u) {
+    const uint32_t lane = threadIdx.x & 63u;
+    for (uint32_t row = blockIdx.x * 4u + (threadIdx.x >> 6); row < a.rows;
+         row += gridDim.x * 4u) {
         const uint64_t* k = a.keys + (uint64_t)row * a.splits;
-        uint64_t best = 0;
-        for (uint32_t s = 0; s < a.splits; ++s) {
-            best = k[s] > best ? k[s] : best;
+        unsigned long long best = 0;
+        for (uint32_t s = lane; s < a.splits; s += 64u) {
+            const unsigned long long v = k[s];
+            best = v > best ? v : best;
         }
-        write_blk(a, row, key_index(best));
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const unsigned long long o = __shfl_xor(best, off);
+            best = o > best ? o : best;
+        }
+        if (lane == 0u) write_blk(a, row, key_index(best));
     }
 }
 
@@ -722,7 +730,7 @@ int run_readout(const uint16_t* base, const uint16_t* bias, const int64_t* cand,
     hipError_t e = launch_plan(a, p, stream);
     if (e != hipSuccess) return hip_fail(e);
     if (p.combine == kTwoPass) {
-        e = launch_reduce_table(a.keys, blk, a.rows, a.bm1, a.splits, stream);
+        e = launch_reduce_table(a.keys, blk, a.cand, a.rows, a.bm1, a.V, a.splits, stream);
         if (e != hipSuccess) return hip_fail(e);
     }
     return XPRESS_OK;
@@ -775,17 +783,18 @@ int workspace_table(hipStream_t stream, int64_t entries, uint64_t** table)
     return XPRESS_OK;
 }
 
-hipError_t launch_reduce_table(uint64_t* table, int64_t* blk, uint32_t rows, uint32_t bm1,
-                               uint32_t splits, hipStream_t stream)
+hipError_t launch_reduce_table(uint64_t* table, int64_t* blk, const int64_t* cand, uint32_t rows,
+                               uint32_t bm1, uint32_t V, uint32_t splits, hipStream_t stream)
 {
     RowArgs a = {};
     a.blk = blk;
     a.rows = rows;
     a.bm1 = bm1;
+    a.V = V;
     a.splits = splits;
     a.keys = table;
-    a.cand = nullptr;
-    const uint32_t grid = (rows + 255u) / 256u < 65536u ? (rows + 255u) / 256u : 65536u;
+    a.cand = cand;
+    const uint32_t grid = (rows + 3u) / 4u < 65536u ? (rows + 3u) / 4u : 65536u;
     hipLaunchKernelGGL(reduce_keys_kernel, dim3(grid), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
