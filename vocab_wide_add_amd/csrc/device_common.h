@@ -142,4 +142,47 @@ __device__ __forceinline__ int64_t key_index(uint64_t key)
     return (int64_t)(kNoIndex - (uint32_t)(key & 0xFFFFFFFFu));
 }
 
+// ---------------------------------------------------------------------------
+// Load-to-LDS and explicit wait counts, for kernels that stream operands into
+// LDS with several loads in flight.
+// ---------------------------------------------------------------------------
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One 16-byte load-to-LDS: lane l's 16 bytes from gsrc land at LDS byte
+// address lds_base + 16 l (lds_base wave-uniform, carried in M0).  Issued as
+// the instructions the compiler itself emits for this load, so that its
+// wait-count pass does not add a wait for every pending load before each LDS
+// read; the contraction loop waits for exactly the chunk it is about to read
+// (wait_vmcnt), and extra loads the compiler places after these only make
+// its own waits stricter.
+__device__ __forceinline__ void dma16(const uint16_t* gsrc, uint32_t lds_base)
+{
+    // M0 is read when the load issues; it is restored right after so that no
+    // other use of M0 sees the LDS address
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(gsrc), "s"(lds_base)
+        : "memory");
+}
+
+// LDS byte address of a __shared__ element, made wave-uniform.
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p)
+{
+    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
+    return __builtin_amdgcn_readfirstlane(a);
+}
+
 }  // namespace xpress

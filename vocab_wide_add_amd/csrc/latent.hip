@@ -436,15 +436,6 @@ constexpr int kKC = 64;           // contraction elements per chunk
 constexpr int kRing = 4;          // chunks in flight
 constexpr int kSlabRows = 128;    // A rows of a staged workgroup
 
-// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // Rows [32 j + 8 w, +8) of a chunk are loaded by wave w's j-th instruction;
 // lane l reads row 32 j + 8 w + l / 8, logical 16-byte column (l % 8) ^ (l / 8),
 // and lands in LDS at row-major position (row, l % 8).
@@ -453,35 +444,6 @@ struct DmaRows {
     static constexpr int kN = ROWS / 32;  // load instructions per wave per chunk
     const uint16_t* src[kN];              // this lane's row, at its swizzled column
 };
-
-// One 16-byte load-to-LDS: lane l's 16 bytes from gsrc land at LDS byte
-// address lds_base + 16 l (lds_base wave-uniform, carried in M0).  Issued as
-// the instructions the compiler itself emits for this load, so that its
-// wait-count pass does not add a wait for every pending load before each LDS
-// read; the contraction loop waits for exactly the chunk it is about to read
-// (wait_vmcnt), and extra loads the compiler places after these only make
-// its own waits stricter.
-__device__ __forceinline__ void dma16(const uint16_t* gsrc, uint32_t lds_base)
-{
-    // M0 is read when the load issues; it is restored right after so that no
-    // other use of M0 sees the LDS address
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(gsrc), "s"(lds_base)
-        : "memory");
-}
-
-// LDS byte address of a __shared__ element, made wave-uniform.
-__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p)
-{
-    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
-    return __builtin_amdgcn_readfirstlane(a);
-}
 
 template <int ROWS>
 __device__ __forceinline__ void dma_chunk(const DmaRows<ROWS>& d, uint16_t* lds_slot, int k0,

@@ -87,6 +87,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
     constexpr int PER_THREAD = CHUNKS / THREADS;
     static_assert(CHUNKS % THREADS == 0, "tile must split evenly over the workgroup");
     __shared__ __attribute__((aligned(16))) unsigned char lds[2][kTileV * ROWB];
+    // base of one full tile for every row of the workgroup, two buffers
+    __shared__ __attribute__((aligned(16))) uint16_t base_lds[2][kWaves * 32 * kTileV];
 
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = threadIdx.x >> 6;
@@ -149,7 +151,37 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
     const uint32_t first_id = t0 * kTileV + 4u * khalf;
     uint32_t bidx = (t0 < t1 && first_id < a.V) ? first_id : kNoIndex;
 
+    // tiles below full_end are full; a ragged vocabulary's last tile is not
+    const uint32_t full_end = (t0 < t1 && t1 * kTileV > a.V) ? t1 - 1u : t1;
+
+    // base of full tiles goes straight into LDS: each wave loads its own 32
+    // rows (instruction j: rows 8j .. 8j+7 of the wave's slab, lane l row
+    // 8j + l/8, logical 16-byte column (l % 8) ^ (l / 8)), so every load
+    // instruction reads eight whole 128-byte row segments, and the wave only
+    // waits for its own loads before its epilogue reads them back
+    const uint16_t* bsrc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t r = (rw * kWaves + wave) * 32u + 8u * j + (lane >> 3);
+        bsrc[j] = a.base + (int64_t)(r < a.rows ? r : 0u) * a.stride_base +
+                  8u * ((lane & 7u) ^ (lane >> 3));
+    }
+    auto dma_base = [&](uint32_t t, uint32_t buf) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            dma16(bsrc[j] + (uint64_t)t * kTileV,
+                  lds_addr(&base_lds[buf][(wave * 32u + 8u * j) * kTileV]));
+        }
+    };
+    // this lane's 4 consecutive ids of run q of slice g, from a staged tile
+    const uint32_t lrow = wave * 32u + (lane & 31u);
+    auto lds_pair = [&](uint32_t buf, int g, int q) -> u32x2 {
+        const uint32_t pc = (uint32_t)(4 * g + q) ^ (lrow & 7u);
+        return *reinterpret_cast<const u32x2*>(&base_lds[buf][lrow * kTileV + pc * 8u + 4u * khalf]);
+    };
+
     if (t0 < t1) {
+        if (t0 < full_end) dma_base(t0, t0 & 1u);
         load_tile(t0);
         store_tile(0);
     }
@@ -158,46 +190,41 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
     // invalid rows read row 0 (always in bounds) and never update
     const uint16_t* brow = a.base + (int64_t)(row_ok ? row : 0u) * a.stride_base;
 
-    // base for one tile: per slice g and run q, the 4 consecutive ids this
-    // lane's accumulators hold.  FULL tiles use plain 8-byte loads; the last
-    // tile of a ragged vocabulary reads each id at min(id, V - 1) -- in
-    // bounds, masked out past V.
-    auto load_base = [&](uint32_t t, u32x2 (&bv)[2][4], auto full_tag) {
-        constexpr bool FULL = decltype(full_tag)::value;
+    // base of the ragged last tile: each id at min(id, V - 1) -- in bounds,
+    // masked out past V
+    auto load_ragged = [&](uint32_t t, u32x2 (&bv)[2][4]) {
         const uint32_t tv = t * kTileV;
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const uint32_t v = tv + 32u * g + 8u * q + 4u * khalf;
-                if constexpr (FULL) {
-                    bv[g][q] = *reinterpret_cast<const u32x2*>(brow + v);
-                } else {
-                    uint32_t e[4];
+                uint32_t e[4];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const uint32_t vj = (v + j < a.V) ? v + j : a.V - 1u;
-                        e[j] = brow[vj];
-                    }
-                    bv[g][q].x = e[0] | (e[1] << 16);
-                    bv[g][q].y = e[2] | (e[3] << 16);
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t vj = (v + j < a.V) ? v + j : a.V - 1u;
+                    e[j] = brow[vj];
                 }
+                bv[g][q].x = e[0] | (e[1] << 16);
+                bv[g][q].y = e[2] | (e[3] << 16);
             }
         }
     };
 
-    // One tile: the next tile's base (when it is a full one) and w loads go
-    // out first and stay in flight; the MFMAs run on the current LDS tile and
-    // the epilogue on base loaded one tile earlier; then the next w tile goes
-    // into the other LDS buffer.
-    auto tile = [&](uint32_t t, u32x2 (&bv)[2][4], u32x2 (&bv_next)[2][4], uint32_t full_end,
-                    auto full_tag) {
+    // One tile: the next tile's base (into LDS) and w (into registers) go out
+    // first and stay in flight; the MFMAs run on the current LDS w tile; the
+    // epilogue waits for this tile's base, loaded one tile earlier; then the
+    // next w tile goes into the other LDS buffer.
+    auto tile = [&](uint32_t t, auto full_tag) {
         constexpr bool FULL = decltype(full_tag)::value;
         const uint32_t cur = (t - t0) & 1u;
         const bool more = t + 1u < t1;
+        const bool next_full = t + 1u < full_end;
         const uint32_t tv = t * kTileV;
-        if (t + 1u < full_end) load_base(t + 1u, bv_next, std::true_type{});
+        if (next_full) dma_base(t + 1u, (t + 1u) & 1u);
         if (more) load_tile(t + 1u);
+        u32x2 bv[2][4];
+        if constexpr (!FULL) load_ragged(t, bv);
 
         // two independent accumulator chains (the tile's two 32-id slices)
         f32x16 acc0 = f32x16{};
@@ -212,6 +239,25 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
                 __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(arow1 + 32 * c));
             acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bx[c], acc0, 0, 0, 0);
             acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bx[c], acc1, 0, 0, 0);
+        }
+
+        if constexpr (FULL) {
+            // this tile's base landed once only the loads issued above are
+            // still outstanding
+            if (next_full && more) {
+                wait_vmcnt<4 + PER_THREAD>();
+            } else if (next_full) {
+                wait_vmcnt<4>();
+            } else if (more) {
+                wait_vmcnt<PER_THREAD>();
+            } else {
+                wait_vmcnt<0>();
+            }
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) bv[g][q] = lds_pair(t & 1u, g, q);
+            }
         }
 
         // epilogue: bias rounded to bf16, added to base, rounded; ascending ids
@@ -241,24 +287,9 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
     };
 
     if (t0 < t1) {
-        // tiles below full_end are full; a ragged vocabulary's last tile is not
-        const uint32_t full_end = (t1 * kTileV <= a.V) ? t1 : t1 - 1u;
-        u32x2 bvA[2][4], bvB[2][4];
-        if (t0 < full_end) load_base(t0, bvA, std::true_type{});
-        // two tiles per trip: the base buffers alternate without copies
         uint32_t t = t0;
-        for (; t + 1u < full_end; t += 2u) {
-            tile(t, bvA, bvB, full_end, std::true_type{});
-            tile(t + 1u, bvB, bvA, full_end, std::true_type{});
-        }
-        if (t < full_end) {
-            tile(t, bvA, bvB, full_end, std::true_type{});
-            ++t;
-        }
-        if (t < t1) {
-            load_base(t, bvA, std::false_type{});
-            tile(t, bvA, bvB, full_end, std::false_type{});
-        }
+        for (; t < full_end; ++t) tile(t, std::true_type{});
+        if (t < t1) tile(t, std::false_type{});
     }
 
     // lanes l and l + 32 hold two halves of the same row's ids
