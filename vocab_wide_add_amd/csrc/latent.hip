@@ -823,9 +823,11 @@ int xpress_latent_pass(const int64_t* blk, const int64_t* am1, const uint16_t* x
         wr_down = rows_u >= kStagedFromRows ? kStaged
                                             : auto_slabs((rows_u + kTile - 1) / kTile * ctiles, cus);
     }
-    // staged gate: two hidden tiles per workgroup when that still fills the chip
     const uint64_t slabs128 = (rows_u + kSlabRows - 1) / kSlabRows;
-    const int gate_nh = (H % 64 == 0 && slabs128 * (uint64_t)(H / 64) >= (uint64_t)cus) ? 2 : 1;
+    // staged gate: two hidden tiles per workgroup once one-tile workgroups
+    // (one per CU: the staging takes most of the LDS) would need two rounds
+    const int gate_nh =
+        (H % 64 == 0 && slabs128 * (uint64_t)(H / 32) > (uint64_t)cus) ? 2 : 1;
     const uint64_t gate_wgs = wr_gate == kStaged
                                   ? slabs128 * (uint64_t)(H / (kTile * gate_nh))
                                   : (rows_u + kTile * wr_gate - 1) / (kTile * wr_gate) * (H / kTile);
