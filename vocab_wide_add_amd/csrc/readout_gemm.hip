@@ -52,8 +52,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kTileV = 64;   // vocabulary ids per tile: two 32-id MFMA slices
-constexpr int kWaves = 8;    // waves (32-row groups) per workgroup
+constexpr int kTileV = 32;   // vocabulary ids per tile: one 32-id MFMA slice
+constexpr int kWaves = 8;    // waves per workgroup
+constexpr int kGroups = 2;   // 32-row groups per wave: they share every A operand read
 
 struct GemmArgs {
     const uint16_t* base;
@@ -84,11 +85,12 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
     constexpr int ROWB = R * 2 + 16;            // bytes per LDS tile row (16 B pad)
     constexpr int CHUNKS = kTileV * R / 8;      // 16-byte chunks per w tile
     constexpr int THREADS = kWaves * 64;
-    constexpr int PER_THREAD = CHUNKS / THREADS;
-    static_assert(CHUNKS % THREADS == 0, "tile must split evenly over the workgroup");
+    constexpr int PER_THREAD = (CHUNKS + THREADS - 1) / THREADS;
+    constexpr int WROWS = 32 * kGroups;         // rows per wave
+    constexpr int BLOADS = WROWS * kTileV * 2 / 1024;  // base copies per wave per tile
     __shared__ __attribute__((aligned(16))) unsigned char lds[2][kTileV * ROWB];
     // base of one full tile for every row of the workgroup, two buffers
-    __shared__ __attribute__((aligned(16))) uint16_t base_lds[2][kWaves * 32 * kTileV];
+    __shared__ __attribute__((aligned(16))) uint16_t base_lds[2][kWaves * WROWS * kTileV];
 
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = threadIdx.x >> 6;
@@ -101,18 +103,29 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
     const uint32_t t0 = (uint32_t)((uint64_t)range * a.tiles / a.ranges);
     const uint32_t t1 = (uint32_t)((uint64_t)(range + 1u) * a.tiles / a.ranges);
 
-    const uint32_t row = (rw * kWaves + wave) * 32u + (lane & 31u);
-    const bool row_ok = row < a.rows;
-
-    // B operands: this lane's draft row of x, 8 of the 16 k of every step
-    bf16x8 bx[KC];
+    // this wave's rows: kGroups groups of 32; the lane's row in group g is
+    // g * 32 + l % 32
+    const uint32_t wrow0 = (rw * kWaves + wave) * WROWS;
+    uint32_t row[kGroups];
+    bool row_ok[kGroups];
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (row_ok) {
-            v = *reinterpret_cast<const u32x4*>(a.x + (uint64_t)row * R + 16 * c + 8 * khalf);
+    for (int g = 0; g < kGroups; ++g) {
+        row[g] = wrow0 + 32u * g + (lane & 31u);
+        row_ok[g] = row[g] < a.rows;
+    }
+
+    // B operands: the lane's draft rows of x, 8 of the 16 k of every step
+    bf16x8 bx[kGroups][KC];
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (row_ok[g]) {
+                v = *reinterpret_cast<const u32x4*>(a.x + (uint64_t)row[g] * R + 16 * c + 8 * khalf);
+            }
+            bx[g][c] = __builtin_bit_cast(bf16x8, v);
         }
-        bx[c] = __builtin_bit_cast(bf16x8, v);
     }
 
     // staging of one w tile: chunk id -> (tile row, 16-byte column)
@@ -125,7 +138,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
             const uint32_t tcol = id % (R / 8);
             const uint32_t v = t * kTileV + trow;
             u32x4 val = {0u, 0u, 0u, 0u};
-            if (v < a.V) {
+            if (id < (uint32_t)CHUNKS && v < a.V) {
                 val = __builtin_nontemporal_load(
                     reinterpret_cast<const u32x4*>(a.w + (uint64_t)v * R) + tcol);
             }
@@ -138,46 +151,51 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
             const uint32_t id = threadIdx.x + i * THREADS;
             const uint32_t trow = id / (R / 8);
             const uint32_t tcol = id % (R / 8);
-            *reinterpret_cast<u32x4*>(&lds[buf][trow * ROWB + tcol * 16]) = stage[i];
+            if (id < (uint32_t)CHUNKS) {
+                *reinterpret_cast<u32x4*>(&lds[buf][trow * ROWB + tcol * 16]) = stage[i];
+            }
         }
     };
 
-    // Running first maximum of this lane's ids.  It starts at the lane's
-    // first id (below V whenever the range has a tile) with value -inf and
-    // only a strictly larger value replaces it, so a lane whose values are
-    // all -inf still reports its first id.  Lanes of rows past the last row
-    // compute on zeros and never publish.
-    float best = -__builtin_inff();
+    // Running first maximum of each of this lane's rows.  It starts at the
+    // lane's first id (below V whenever the range has a tile) with value -inf
+    // and only a strictly larger value replaces it, so a lane whose values
+    // are all -inf still reports its first id.  Lanes of rows past the last
+    // row compute on zeros and never publish.
     const uint32_t first_id = t0 * kTileV + 4u * khalf;
-    uint32_t bidx = (t0 < t1 && first_id < a.V) ? first_id : kNoIndex;
+    float best[kGroups];
+    uint32_t bidx[kGroups];
+    const uint16_t* brow[kGroups];
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+        best[g] = -__builtin_inff();
+        bidx[g] = (t0 < t1 && first_id < a.V) ? first_id : kNoIndex;
+        // invalid rows read row 0 (always in bounds) and never update
+        brow[g] = a.base + (int64_t)(row_ok[g] ? row[g] : 0u) * a.stride_base;
+    }
 
     // tiles below full_end are full; a ragged vocabulary's last tile is not
     const uint32_t full_end = (t0 < t1 && t1 * kTileV > a.V) ? t1 - 1u : t1;
 
-    // base of full tiles goes straight into LDS: each wave loads its own 32
-    // rows (instruction j: rows 8j .. 8j+7 of the wave's slab, lane l row
-    // 8j + l/8, logical 16-byte column (l % 8) ^ (l / 8)), so every load
-    // instruction reads eight whole 128-byte row segments, and the wave only
-    // waits for its own loads before its epilogue reads them back
-    const uint16_t* bsrc[4];
+    // base of full tiles goes straight into LDS: each wave copies its own
+    // rows (instruction j: rows 16j .. 16j+15 of the wave's, lane l row
+    // 16j + l/4, logical 16-byte column (l % 4) ^ (row % 4)), so a load
+    // instruction reads sixteen 64-byte row segments, and the wave only
+    // waits for its own copies before its epilogue reads them back
+    const uint16_t* bsrc[BLOADS];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t r = (rw * kWaves + wave) * 32u + 8u * j + (lane >> 3);
+    for (int j = 0; j < BLOADS; ++j) {
+        const uint32_t rl = 16u * j + (lane >> 2);
+        const uint32_t r = wrow0 + rl;
         bsrc[j] = a.base + (int64_t)(r < a.rows ? r : 0u) * a.stride_base +
-                  8u * ((lane & 7u) ^ (lane >> 3));
+                  8u * ((lane & 3u) ^ (rl & 3u));
     }
     auto dma_base = [&](uint32_t t, uint32_t buf) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < BLOADS; ++j) {
             dma16(bsrc[j] + (uint64_t)t * kTileV,
-                  lds_addr(&base_lds[buf][(wave * 32u + 8u * j) * kTileV]));
+                  lds_addr(&base_lds[buf][(wave * WROWS + 16u * j) * kTileV]));
         }
-    };
-    // this lane's 4 consecutive ids of run q of slice g, from a staged tile
-    const uint32_t lrow = wave * 32u + (lane & 31u);
-    auto lds_pair = [&](uint32_t buf, int g, int q) -> u32x2 {
-        const uint32_t pc = (uint32_t)(4 * g + q) ^ (lrow & 7u);
-        return *reinterpret_cast<const u32x2*>(&base_lds[buf][lrow * kTileV + pc * 8u + 4u * khalf]);
     };
 
     if (t0 < t1) {
@@ -187,33 +205,9 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
     }
     __syncthreads();
 
-    // invalid rows read row 0 (always in bounds) and never update
-    const uint16_t* brow = a.base + (int64_t)(row_ok ? row : 0u) * a.stride_base;
-
-    // base of the ragged last tile: each id at min(id, V - 1) -- in bounds,
-    // masked out past V
-    auto load_ragged = [&](uint32_t t, u32x2 (&bv)[2][4]) {
-        const uint32_t tv = t * kTileV;
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t v = tv + 32u * g + 8u * q + 4u * khalf;
-                uint32_t e[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t vj = (v + j < a.V) ? v + j : a.V - 1u;
-                    e[j] = brow[vj];
-                }
-                bv[g][q].x = e[0] | (e[1] << 16);
-                bv[g][q].y = e[2] | (e[3] << 16);
-            }
-        }
-    };
-
     // One tile: the next tile's base (into LDS) and w (into registers) go out
     // first and stay in flight; the MFMAs run on the current LDS w tile; the
-    // epilogue waits for this tile's base, loaded one tile earlier; then the
+    // epilogue waits for this tile's base, copied one tile earlier; then the
     // next w tile goes into the other LDS buffer.
     auto tile = [&](uint32_t t, auto full_tag) {
         constexpr bool FULL = decltype(full_tag)::value;
@@ -223,61 +217,79 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
         const uint32_t tv = t * kTileV;
         if (next_full) dma_base(t + 1u, (t + 1u) & 1u);
         if (more) load_tile(t + 1u);
-        u32x2 bv[2][4];
-        if constexpr (!FULL) load_ragged(t, bv);
+        u32x2 bv[kGroups][4];
+        if constexpr (!FULL) {
+            // each id at min(id, V - 1): in bounds, masked out past V
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t v = tv + 8u * q + 4u * khalf;
+                    uint32_t e[4];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) e[jj] = brow[g][(v + jj < a.V) ? v + jj : a.V - 1u];
+                    bv[g][q].x = e[0] | (e[1] << 16);
+                    bv[g][q].y = e[2] | (e[3] << 16);
+                }
+            }
+        }
 
-        // two independent accumulator chains (the tile's two 32-id slices)
-        f32x16 acc0 = f32x16{};
-        f32x16 acc1 = f32x16{};
-        const unsigned char* arow0 = &lds[cur][(lane & 31u) * ROWB + 16u * khalf];
-        const unsigned char* arow1 = arow0 + 32 * ROWB;
+        // one A operand read feeds the kGroups independent accumulator chains
+        f32x16 acc[kGroups];
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) acc[g] = f32x16{};
+        const unsigned char* arow = &lds[cur][(lane & 31u) * ROWB + 16u * khalf];
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
             const bf16x8 a0 =
-                __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(arow0 + 32 * c));
-            const bf16x8 a1 =
-                __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(arow1 + 32 * c));
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bx[c], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bx[c], acc1, 0, 0, 0);
+                __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(arow + 32 * c));
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g) {
+                acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bx[g][c], acc[g], 0, 0, 0);
+            }
         }
 
         if constexpr (FULL) {
-            // this tile's base landed once only the loads issued above are
-            // still outstanding
+            // this tile's base landed once only the loads issued above remain
             if (next_full && more) {
-                wait_vmcnt<4 + PER_THREAD>();
+                wait_vmcnt<BLOADS + PER_THREAD>();
             } else if (next_full) {
-                wait_vmcnt<4>();
+                wait_vmcnt<BLOADS>();
             } else if (more) {
                 wait_vmcnt<PER_THREAD>();
             } else {
                 wait_vmcnt<0>();
             }
 #pragma unroll
-            for (int g = 0; g < 2; ++g) {
+            for (int g = 0; g < kGroups; ++g) {
+                const uint32_t lrow = wave * WROWS + 32u * g + (lane & 31u);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) bv[g][q] = lds_pair(t & 1u, g, q);
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t pc = (uint32_t)q ^ (lrow & 3u);
+                    bv[g][q] = *reinterpret_cast<const u32x2*>(
+                        &base_lds[t & 1u][lrow * kTileV + pc * 8u + 4u * khalf]);
+                }
             }
         }
 
         // epilogue: bias rounded to bf16, added to base, rounded; ascending ids
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            const f32x16& acc = g ? acc1 : acc0;
+        for (int g = 0; g < kGroups; ++g) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const uint32_t v = tv + 32u * g + 8u * q + 4u * khalf;
-                const uint32_t s01 = add_round2(bv[g][q].x,
-                                                round_pack2(acc[4 * q], acc[4 * q + 1]));
-                const uint32_t s23 = add_round2(bv[g][q].y,
-                                                round_pack2(acc[4 * q + 2], acc[4 * q + 3]));
+                const uint32_t v = tv + 8u * q + 4u * khalf;
+                const uint32_t s01 =
+                    add_round2(bv[g][q].x, round_pack2(acc[g][4 * q], acc[g][4 * q + 1]));
+                const uint32_t s23 =
+                    add_round2(bv[g][q].y, round_pack2(acc[g][4 * q + 2], acc[g][4 * q + 3]));
                 const float sv[4] = {bf16_lo(s01), bf16_hi(s01), bf16_lo(s23), bf16_hi(s23)};
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int jj = 0; jj < 4; ++jj) {
                     // ids past V exist only in a ragged last tile
-                    const bool take = FULL ? (sv[j] > best) : ((v + j < a.V) && (sv[j] > best));
-                    best = take ? sv[j] : best;
-                    bidx = take ? v + j : bidx;
+                    const bool take =
+                        FULL ? (sv[jj] > best[g]) : ((v + jj < a.V) && (sv[jj] > best[g]));
+                    best[g] = take ? sv[jj] : best[g];
+                    bidx[g] = take ? v + jj : bidx[g];
                 }
             }
         }
@@ -293,11 +305,14 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
     }
 
     // lanes l and l + 32 hold two halves of the same row's ids
-    const float ov = __shfl_xor(best, 32);
-    const uint32_t oi = __shfl_xor(bidx, 32);
-    merge(best, bidx, ov, oi);
-    if (khalf == 0u && row_ok) {
-        a.table[(uint64_t)row * a.ranges + range] = make_key(best, bidx);
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+        const float ov = __shfl_xor(best[g], 32);
+        const uint32_t oi = __shfl_xor(bidx[g], 32);
+        merge(best[g], bidx[g], ov, oi);
+        if (khalf == 0u && row_ok[g]) {
+            a.table[(uint64_t)row[g] * a.ranges + range] = make_key(best[g], bidx[g]);
+        }
     }
 }
 
@@ -344,7 +359,7 @@ extern "C" int xpress_readout_gemm_argmax_to_blk(const uint16_t* base, const uin
     a.V = (uint32_t)V;
     a.tiles = (uint32_t)((V + kTileV - 1) / kTileV);
     const int64_t groups = (rows + 31) / 32;
-    a.row_wgs = (uint32_t)((groups + kWaves - 1) / kWaves);
+    a.row_wgs = (uint32_t)((groups + kWaves * kGroups - 1) / (kWaves * kGroups));
     // about one workgroup per CU (a workgroup fills its CU's LDS and two
     // waves per SIMD); ranges a multiple of 8 (one per XCD slot)
     int64_t ranges = (int64_t)device_cus() / a.row_wgs;
