@@ -140,6 +140,13 @@ def time_graph(step, steps: int, warmup: int, per_graph: int, reserve):
     return wall, r0.elapsed_time(r1) * 1e-3, reps * per_graph
 
 
+def last_set(args, sets: int) -> int:
+    """Input set written by the last timed step: step k uses set k % sets; a
+    captured graph replays steps 0 .. per_graph - 1."""
+    last = (args.graph if args.graph else args.steps) - 1
+    return last % sets
+
+
 def time_steps(step, steps: int, warmup: int, stream):
     """Warm up, then time ``steps`` calls twice: region 1 back to back (wall
     clock and one HIP event pair on the launch stream around the region),
@@ -240,7 +247,7 @@ def bench_readout(args, np, torch, native, workloads):
         durs = [region_gpu / n]
     else:
         wall, region_gpu, durs = time_steps(step, args.steps, args.warmup, stream)
-    got = dev[(args.steps - 1) % sets][2].cpu().numpy()
+    got = dev[last_set(args, sets)][2].cpu().numpy()
     config = {"workload": name, "N": w.N, "B": w.B, "V": w.V, "rows": w.rows,
               "stride_base": w.stride_base, "stride_bias": w.stride_bias,
               "bytes_per_step": w.bytes_read, "input_sets": sets, "plan": plan,
@@ -295,7 +302,7 @@ def bench_topc(args, np, torch, native, workloads):
     out = result_line("top-C readout: effective GB/s and rows/s, N=%d B=%d C=%d"
                       % (w.N, w.B, w.C), name, config, w.bytes_read, w.rows, args.steps,
                       args.warmup, wall, region_gpu, durs, plan["launches"], None)
-    got = dev[(args.steps - 1) % sets][3].cpu().numpy()
+    got = dev[last_set(args, sets)][3].cpu().numpy()
     if not args.no_cpu_baseline:
         import oracle
         log("cpu baseline")
@@ -335,6 +342,8 @@ def bench_gemm(args, np, torch, native, workloads):
                                                  stream=st)
 
     wall, region_gpu, durs = time_steps(step, args.steps, args.warmup, stream)
+    # the fused path's answers, before the unfused context path reuses blk
+    got = dev[last_set(args, sets)][3].cpu().numpy()[:, 1:].reshape(-1)
     config = {"workload": name, "op": "readout_gemm", "N": w.N, "B": w.B, "V": w.V, "R": w.R,
               "rows": w.rows, "bytes_per_step": w.bytes_read, "flops_per_step": w.flops,
               "input_sets": sets}
@@ -361,7 +370,6 @@ def bench_gemm(args, np, torch, native, workloads):
     if not args.no_cpu_baseline:
         import oracle
         log("cpu baseline")
-        got = dev[(args.steps - 1) % sets][3].cpu().numpy()[:, 1:].reshape(-1)
         cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else 1
         n = max(cores, 16)
         rows = list(range(0, w.rows, max(1, w.rows // n)))[:n]
