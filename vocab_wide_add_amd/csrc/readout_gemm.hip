@@ -19,12 +19,18 @@
 //     slice of w), the draft rows along N (B operand = x^T): each lane's 16
 //     accumulators are then 4 runs of 4 consecutive ids of ONE draft row,
 //     which is what the epilogue's running maximum wants;
-//   * a wave owns 32 draft rows; their x rows (R bf16 each) stay in
-//     registers as the B operands for the whole launch;
-//   * a workgroup of kWaves waves covers 32*kWaves rows and a contiguous range
-//     of 64-id tiles; each tile of w is staged through registers into a
-//     padded, double-buffered LDS tile shared by the waves, the next tile's
-//     loads in flight while the current one is multiplied;
+//   * a wave owns 64 draft rows (two 32-row groups whose matrix instructions
+//     share every A-operand read); their x rows stay in registers as the B
+//     operands for the whole launch;
+//   * a workgroup of 8 waves covers 512 rows and a contiguous range of
+//     32-id tiles; w tiles and each wave's base tiles are copied straight
+//     into LDS by the 16-byte load-to-LDS instruction, two tiles ahead in
+//     rings of three, and each wave waits only on its own copies (explicit
+//     counts) before the one barrier per tile;
+//   * all waves run the same phase together (matrix instructions, then the
+//     epilogue): measured on this part, a SIMD's two waves retire matrix
+//     instructions faster together than one alone, and vector instructions
+//     likewise, while the two kinds from different waves slow each other;
 //   * the workgroups that cover the row groups of one vocabulary range are
 //     placed on one XCD (workgroup b runs on XCD b mod 8), so each w tile is
 //     fetched from HBM once and served from that XCD's L2 afterwards;
@@ -55,6 +61,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kTileV = 32;   // vocabulary ids per tile: one 32-id MFMA slice
 constexpr int kWaves = 8;    // waves per workgroup
 constexpr int kGroups = 2;   // 32-row groups per wave: they share every A operand read
+constexpr int kRing = 3;     // w tiles and base tiles resident in LDS
+constexpr int kAhead = 4;    // A-operand registers: reads run three steps ahead
 
 struct GemmArgs {
     const uint16_t* base;
@@ -78,22 +86,53 @@ __device__ __forceinline__ uint32_t round_pack2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(s, bf16x2));
 }
 
+// s_waitcnt vmcnt(n) for a wave-uniform n known only at run time (the
+// instruction takes an immediate); n above the largest case waits for all.
+__device__ __forceinline__ void wait_vmcnt_dyn(int n)
+{
+    switch (n) {
+        case 14: wait_vmcnt<14>(); break;
+        case 13: wait_vmcnt<13>(); break;
+        case 12: wait_vmcnt<12>(); break;
+        case 11: wait_vmcnt<11>(); break;
+        case 10: wait_vmcnt<10>(); break;
+        case 9: wait_vmcnt<9>(); break;
+        case 8: wait_vmcnt<8>(); break;
+        case 7: wait_vmcnt<7>(); break;
+        case 6: wait_vmcnt<6>(); break;
+        case 5: wait_vmcnt<5>(); break;
+        case 4: wait_vmcnt<4>(); break;
+        case 3: wait_vmcnt<3>(); break;
+        case 2: wait_vmcnt<2>(); break;
+        case 1: wait_vmcnt<1>(); break;
+        default: wait_vmcnt<0>(); break;
+    }
+}
+
 template <int R>
 __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
 {
     constexpr int KC = R / 16;                  // MFMA steps over k
-    constexpr int ROWB = R * 2 + 16;            // bytes per LDS tile row (16 B pad)
-    constexpr int CHUNKS = kTileV * R / 8;      // 16-byte chunks per w tile
-    constexpr int THREADS = kWaves * 64;
-    constexpr int PER_THREAD = (CHUNKS + THREADS - 1) / THREADS;
+    constexpr int ROWB = R * 2;                 // bytes per w row in LDS
+    constexpr int CPR = R / 8;                  // 16-byte chunks per w row
+    constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;  // chunk swizzle mask
+    constexpr int WBYTES = kTileV * ROWB;       // one w tile
+    constexpr int TW = WBYTES / 1024;           // load-to-LDS copies per w tile
+    constexpr int WPW = TW >= kWaves ? TW / kWaves : 1;  // copies per issuing wave
     constexpr int WROWS = 32 * kGroups;         // rows per wave
     constexpr int BLOADS = WROWS * kTileV * 2 / 1024;  // base copies per wave per tile
-    __shared__ __attribute__((aligned(16))) unsigned char lds[2][kTileV * ROWB];
-    // base of one full tile for every row of the workgroup, two buffers
-    __shared__ __attribute__((aligned(16))) uint16_t base_lds[2][kWaves * WROWS * kTileV];
+    static_assert(WPW * kWaves == TW || (TW < kWaves && WPW == 1 && kWaves % TW == 0),
+                  "w copies split over waves");
+    static_assert(BLOADS * 1024 == WROWS * kTileV * 2, "base copies cover the wave's rows");
+    // w tiles: row i (one id) at i * ROWB, its 16-byte chunk j at position
+    // j ^ (i & SWZ), so the 16 rows one matrix-operand read touches sit in 16
+    // different bank groups
+    __shared__ __attribute__((aligned(1024))) unsigned char w_lds[kRing][WBYTES];
+    // base of one full tile for each wave's rows
+    __shared__ __attribute__((aligned(16))) uint16_t base_lds[kRing][kWaves * WROWS * kTileV];
 
     const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t wave = threadIdx.x >> 6;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t khalf = lane >> 5;
     const uint32_t b = blockIdx.x;
     const uint32_t xcd = b & 7u;
@@ -102,10 +141,16 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
     const uint32_t rw = local % a.row_wgs;
     const uint32_t t0 = (uint32_t)((uint64_t)range * a.tiles / a.ranges);
     const uint32_t t1 = (uint32_t)((uint64_t)(range + 1u) * a.tiles / a.ranges);
+    const int T = (int)(t1 - t0);
+    // tiles below Tfull are full; a ragged vocabulary's last tile is not
+    const int Tfull = (T > 0 && t1 * kTileV > a.V) ? T - 1 : T;
 
     // this wave's rows: kGroups groups of 32; the lane's row in group g is
-    // g * 32 + l % 32
-    const uint32_t wrow0 = (rw * kWaves + wave) * WROWS;
+    // g * 32 + l % 32.  The slab a wave takes rotates with the workgroup's
+    // slot on its XCD, so the compute units of one XCD, which all load every
+    // x row at start, do not all ask for the same rows at the same time.
+    const uint32_t slab = (wave + local) % (uint32_t)kWaves;
+    const uint32_t wrow0 = (rw * kWaves + slab) * WROWS;
     uint32_t row[kGroups];
     bool row_ok[kGroups];
 #pragma unroll
@@ -113,6 +158,66 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
         row[g] = wrow0 + 32u * g + (lane & 31u);
         row_ok[g] = row[g] < a.rows;
     }
+
+    // --- copies into LDS -------------------------------------------------
+    // Source addresses are formed at each copy (a few integer operations per
+    // copy) rather than kept in registers, which the x operands fill.
+    // base: each wave copies its own rows (instruction j: rows 16j .. 16j+15
+    // of the wave's, lane l row 16j + l/4, logical 16-byte column
+    // (l % 4) ^ (row % 4)); only that wave reads them back.  Rows past the
+    // last read the last row and are never used.
+    const uint32_t b_lrow = lane >> 2;
+    const uint32_t b_col = 8u * ((lane & 3u) ^ (b_lrow & 3u));
+    auto dma_base = [&](uint32_t t, int buf) {
+#pragma unroll
+        for (int j = 0; j < BLOADS; ++j) {
+            uint32_t r = wrow0 + 16u * j + b_lrow;
+            r = r < a.rows ? r : a.rows - 1u;
+            dma16(a.base + (uint64_t)r * (uint64_t)a.stride_base + b_col + (uint64_t)t * kTileV,
+                  lds_addr(&base_lds[buf][(wave * WROWS + 16u * j) * kTileV]));
+        }
+    };
+    // w: copy m of a tile fills LDS bytes [1024 m, 1024 m + 1024) with 64
+    // chunks (tile row q / CPR, position q % CPR for q = 64 m + lane); wave
+    // w issues copies (w * WPW + k) mod TW (at R = 64 the last four waves
+    // repeat the first four's, so that every wave issues the same count)
+    auto dma_w = [&](uint32_t t, int buf) {
+#pragma unroll
+        for (int k = 0; k < WPW; ++k) {
+            const uint32_t m = (wave * WPW + k) % (uint32_t)TW;
+            const uint32_t q = 64u * m + lane;
+            const uint32_t i = q / CPR;
+            const uint32_t p = q % CPR;
+            uint32_t v = t * kTileV + i;
+            v = v < a.V ? v : a.V - 1u;        // ids past V: any row, masked later
+            dma16(a.w + (uint64_t)v * R + 8u * (p ^ (i & (uint32_t)SWZ)),
+                  lds_addr(reinterpret_cast<const uint16_t*>(&w_lds[buf][1024u * m])));
+        }
+    };
+
+    // Copy schedule: at the start of tile j every wave copies base tile j + 2
+    // (if full) and its share of w tile j + 2, two tiles ahead in a ring of
+    // three; the copies of tiles -2 and -1 go out before the loop.  n(j)
+    // counts the wave's copies at tile j; the wait at the end of tile j
+    // (everything but tile j's own copies) lands tile j + 1 for the barrier.
+    auto n_copies = [&](int j) -> int {
+        const int tt = j + 2;
+        if (tt < 0 || tt >= T) return 0;
+        return (tt < Tfull ? BLOADS : 0) + WPW;
+    };
+    auto issue_base = [&](int j) {
+        const int tt = j + 2;
+        if (tt >= 0 && tt < Tfull) dma_base(t0 + (uint32_t)tt, tt % kRing);
+    };
+    auto issue_w = [&](int j) {
+        const int tt = j + 2;
+        if (tt >= 0 && tt < T) dma_w(t0 + (uint32_t)tt, tt % kRing);
+    };
+    auto issue = [&](int j) {
+        issue_base(j);
+        issue_w(j);
+    };
+    issue(-2);
 
     // B operands: the lane's draft rows of x, 8 of the 16 k of every step
     bf16x8 bx[kGroups][KC];
@@ -127,191 +232,164 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
             bx[g][c] = __builtin_bit_cast(bf16x8, v);
         }
     }
+    // Tile 0's copies and x have landed.  Waiting for all of it here also
+    // tells the compiler so; otherwise it cannot prove the conditional x
+    // loads complete and waits for every copy in flight before the first
+    // matrix instruction of each tile.
+    wait_vmcnt<0>();
+    issue(-1);
 
-    // staging of one w tile: chunk id -> (tile row, 16-byte column)
-    u32x4 stage[PER_THREAD];
-    auto load_tile = [&](uint32_t t) {
-#pragma unroll
-        for (int i = 0; i < PER_THREAD; ++i) {
-            const uint32_t id = threadIdx.x + i * THREADS;
-            const uint32_t trow = id / (R / 8);
-            const uint32_t tcol = id % (R / 8);
-            const uint32_t v = t * kTileV + trow;
-            u32x4 val = {0u, 0u, 0u, 0u};
-            if (id < (uint32_t)CHUNKS && v < a.V) {
-                val = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4*>(a.w + (uint64_t)v * R) + tcol);
-            }
-            stage[i] = val;
-        }
-    };
-    auto store_tile = [&](uint32_t buf) {
-#pragma unroll
-        for (int i = 0; i < PER_THREAD; ++i) {
-            const uint32_t id = threadIdx.x + i * THREADS;
-            const uint32_t trow = id / (R / 8);
-            const uint32_t tcol = id % (R / 8);
-            if (id < (uint32_t)CHUNKS) {
-                *reinterpret_cast<u32x4*>(&lds[buf][trow * ROWB + tcol * 16]) = stage[i];
-            }
-        }
-    };
-
-    // Running first maximum of each of this lane's rows.  It starts at the
-    // lane's first id (below V whenever the range has a tile) with value -inf
-    // and only a strictly larger value replaces it, so a lane whose values
-    // are all -inf still reports its first id.  Lanes of rows past the last
-    // row compute on zeros and never publish.
+    // Running first maximum of each of this lane's rows, ids held relative
+    // to t0 * kTileV + 4 khalf (tile-uniform candidates, no per-lane id
+    // registers).  It starts at the lane's first id (below V whenever the
+    // range has a tile) with value -inf and only a strictly larger value
+    // replaces it, so a lane whose values are all -inf still reports its
+    // first id.  Lanes of rows past the last row never publish.
     const uint32_t first_id = t0 * kTileV + 4u * khalf;
     float best[kGroups];
     uint32_t bidx[kGroups];
-    const uint16_t* brow[kGroups];
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) {
         best[g] = -__builtin_inff();
-        bidx[g] = (t0 < t1 && first_id < a.V) ? first_id : kNoIndex;
-        // invalid rows read row 0 (always in bounds) and never update
-        brow[g] = a.base + (int64_t)(row_ok[g] ? row[g] : 0u) * a.stride_base;
+        bidx[g] = (T > 0 && first_id < a.V) ? 0u : kNoIndex;
     }
 
-    // tiles below full_end are full; a ragged vocabulary's last tile is not
-    const uint32_t full_end = (t0 < t1 && t1 * kTileV > a.V) ? t1 - 1u : t1;
-
-    // base of full tiles goes straight into LDS: each wave copies its own
-    // rows (instruction j: rows 16j .. 16j+15 of the wave's, lane l row
-    // 16j + l/4, logical 16-byte column (l % 4) ^ (row % 4)), so a load
-    // instruction reads sixteen 64-byte row segments, and the wave only
-    // waits for its own copies before its epilogue reads them back
-    const uint16_t* bsrc[BLOADS];
-#pragma unroll
-    for (int j = 0; j < BLOADS; ++j) {
-        const uint32_t rl = 16u * j + (lane >> 2);
-        const uint32_t r = wrow0 + rl;
-        bsrc[j] = a.base + (int64_t)(r < a.rows ? r : 0u) * a.stride_base +
-                  8u * ((lane & 3u) ^ (rl & 3u));
-    }
-    auto dma_base = [&](uint32_t t, uint32_t buf) {
-#pragma unroll
-        for (int j = 0; j < BLOADS; ++j) {
-            dma16(bsrc[j] + (uint64_t)t * kTileV,
-                  lds_addr(&base_lds[buf][(wave * WROWS + 16u * j) * kTileV]));
-        }
-    };
-
-    if (t0 < t1) {
-        if (t0 < full_end) dma_base(t0, t0 & 1u);
-        load_tile(t0);
-        store_tile(0);
-    }
-    __syncthreads();
-
-    // One tile: the next tile's base (into LDS) and w (into registers) go out
-    // first and stay in flight; the MFMAs run on the current LDS w tile; the
-    // epilogue waits for this tile's base, copied one tile earlier; then the
-    // next w tile goes into the other LDS buffer.
-    auto tile = [&](uint32_t t, auto full_tag) {
+    f32x16 acc[kGroups];
+    // Base of group g's rows in tile i, four consecutive ids per entry: from
+    // LDS for a full tile, straight from memory for the ragged last tile
+    // (each id at min(id, V - 1); rows past the last read row 0 and never
+    // publish).
+    auto load_bv = [&](int g, int i, uint32_t tv, auto full_tag, u32x2 (&bv)[4]) {
         constexpr bool FULL = decltype(full_tag)::value;
-        const uint32_t cur = (t - t0) & 1u;
-        const bool more = t + 1u < t1;
-        const bool next_full = t + 1u < full_end;
-        const uint32_t tv = t * kTileV;
-        if (next_full) dma_base(t + 1u, (t + 1u) & 1u);
-        if (more) load_tile(t + 1u);
-        u32x2 bv[kGroups][4];
-        if constexpr (!FULL) {
-            // each id at min(id, V - 1): in bounds, masked out past V
-#pragma unroll
-            for (int g = 0; g < kGroups; ++g) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t v = tv + 8u * q + 4u * khalf;
-                    uint32_t e[4];
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) e[jj] = brow[g][(v + jj < a.V) ? v + jj : a.V - 1u];
-                    bv[g][q].x = e[0] | (e[1] << 16);
-                    bv[g][q].y = e[2] | (e[3] << 16);
-                }
-            }
-        }
-
-        // one A operand read feeds the kGroups independent accumulator chains
-        f32x16 acc[kGroups];
-#pragma unroll
-        for (int g = 0; g < kGroups; ++g) acc[g] = f32x16{};
-        const unsigned char* arow = &lds[cur][(lane & 31u) * ROWB + 16u * khalf];
-#pragma unroll
-        for (int c = 0; c < KC; ++c) {
-            const bf16x8 a0 =
-                __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(arow + 32 * c));
-#pragma unroll
-            for (int g = 0; g < kGroups; ++g) {
-                acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bx[g][c], acc[g], 0, 0, 0);
-            }
-        }
-
         if constexpr (FULL) {
-            // this tile's base landed once only the loads issued above remain
-            if (next_full && more) {
-                wait_vmcnt<BLOADS + PER_THREAD>();
-            } else if (next_full) {
-                wait_vmcnt<BLOADS>();
-            } else if (more) {
-                wait_vmcnt<PER_THREAD>();
-            } else {
-                wait_vmcnt<0>();
+            const uint32_t lrow = wave * WROWS + 32u * g + (lane & 31u);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t pc = (uint32_t)q ^ (lrow & 3u);
+                bv[q] = *reinterpret_cast<const u32x2*>(
+                    &base_lds[i % kRing][lrow * kTileV + pc * 8u + 4u * khalf]);
             }
-#pragma unroll
-            for (int g = 0; g < kGroups; ++g) {
-                const uint32_t lrow = wave * WROWS + 32u * g + (lane & 31u);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t pc = (uint32_t)q ^ (lrow & 3u);
-                    bv[g][q] = *reinterpret_cast<const u32x2*>(
-                        &base_lds[t & 1u][lrow * kTileV + pc * 8u + 4u * khalf]);
-                }
-            }
-        }
-
-        // epilogue: bias rounded to bf16, added to base, rounded; ascending ids
-#pragma unroll
-        for (int g = 0; g < kGroups; ++g) {
+        } else {
+            const uint16_t* brow = a.base + (int64_t)(row_ok[g] ? row[g] : 0u) * a.stride_base;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const uint32_t v = tv + 8u * q + 4u * khalf;
+                uint32_t e[4];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) e[jj] = brow[(v + jj < a.V) ? v + jj : a.V - 1u];
+                bv[q].x = e[0] | (e[1] << 16);
+                bv[q].y = e[2] | (e[3] << 16);
+            }
+        }
+    };
+
+    const uint32_t arow = lane & 31u;
+    const uint32_t aswz = (khalf ^ (arow & (uint32_t)SWZ));
+    __syncthreads();
+    // One tile: copies two tiles ahead; the matrix instructions on w tile i
+    // (one A-operand read feeds both row groups); the epilogue (bias rounded
+    // to bf16, added to base, rounded, compared); then the wait that lands
+    // tile i + 1 and the barrier.  All waves run the same phase together: on
+    // this part a SIMD's two waves issue matrix instructions faster together
+    // than one alone, and vector instructions likewise, while the two kinds
+    // from different waves slow each other down.  Full tiles run in the loop;
+    // a ragged last tile runs after it, where x is no longer live, so its
+    // clamped loads do not compete with x for registers.
+    auto step = [&](int i, auto full_tag, auto steady_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        // steady: tile i + 2 exists and is full, so the copies and the wait
+        // count are the fixed ones and the body has no branches
+        constexpr bool STEADY = decltype(steady_tag)::value;
+        const uint32_t tv = (t0 + (uint32_t)i) * kTileV;
+        // base copies now, w copies between the two groups' epilogues: each
+        // wave's copies go to the address unit in two smaller bursts
+        if constexpr (STEADY) {
+            dma_base(t0 + (uint32_t)(i + 2), (i + 2) % kRing);
+        } else {
+            issue_base(i);
+        }
+        const unsigned char* wrow = &w_lds[i % kRing][arow * ROWB];
+        // logical chunk 2c + khalf of the lane's w row sits at position
+        // (2c + khalf) ^ (row & SWZ)
+        auto a_op = [&](int c) {
+            const uint32_t pos = (2u * c) ^ aswz;
+            return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(wrow + 16u * pos));
+        };
+        // A operands read kAhead steps ahead into rotating registers; one read
+        // feeds both row groups' matrix instructions; a scheduling barrier
+        // after each step keeps that order.
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) acc[g] = f32x16{};
+        bf16x8 ar[kAhead];
+#pragma unroll
+        for (int c = 0; c < kAhead - 1 && c < KC; ++c) ar[c] = a_op(c);
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            if (c + kAhead - 1 < KC) ar[(c + kAhead - 1) % kAhead] = a_op(c + kAhead - 1);
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g) {
+                acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[c % kAhead], bx[g][c], acc[g],
+                                                                 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // The epilogue starts after the last matrix instruction: the vector
+        // work is not spread between them (on this part vector and matrix
+        // instructions interleaved in one wave slow each other beyond a few
+        // per step).
+        asm volatile("" : "+v"(acc[0]), "+v"(acc[1]));
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) {
+            if (g == 1) {
+                if constexpr (STEADY) {
+                    dma_w(t0 + (uint32_t)(i + 2), (i + 2) % kRing);
+                } else {
+                    issue_w(i);
+                }
+            }
+            u32x2 bv[4];
+            load_bv(g, i, tv, full_tag, bv);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
                 const uint32_t s01 =
-                    add_round2(bv[g][q].x, round_pack2(acc[g][4 * q], acc[g][4 * q + 1]));
+                    add_round2(bv[q].x, round_pack2(acc[g][4 * q], acc[g][4 * q + 1]));
                 const uint32_t s23 =
-                    add_round2(bv[g][q].y, round_pack2(acc[g][4 * q + 2], acc[g][4 * q + 3]));
+                    add_round2(bv[q].y, round_pack2(acc[g][4 * q + 2], acc[g][4 * q + 3]));
                 const float sv[4] = {bf16_lo(s01), bf16_hi(s01), bf16_lo(s23), bf16_hi(s23)};
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     // ids past V exist only in a ragged last tile
                     const bool take =
-                        FULL ? (sv[jj] > best[g]) : ((v + jj < a.V) && (sv[jj] > best[g]));
+                        FULL ? (sv[jj] > best[g])
+                             : ((tv + 8u * q + 4u * khalf + jj < a.V) && (sv[jj] > best[g]));
                     best[g] = take ? sv[jj] : best[g];
-                    bidx[g] = take ? v + jj : bidx[g];
+                    bidx[g] = take ? (uint32_t)(kTileV * i + 8 * q + jj) : bidx[g];
                 }
             }
         }
-
-        if (more) store_tile(cur ^ 1u);
+        // tile i + 1 went out at tile i - 1; only tile i's copies may remain
+        if constexpr (STEADY) {
+            wait_vmcnt<BLOADS + WPW>();
+        } else {
+            if (i + 1 < T) wait_vmcnt_dyn(n_copies(i));
+        }
         __syncthreads();
     };
+    int i = 0;
+    for (; i + 2 < Tfull; ++i) step(i, std::true_type{}, std::true_type{});
+    for (; i < Tfull; ++i) step(i, std::true_type{}, std::false_type{});
+    if (Tfull < T) step(T - 1, std::false_type{}, std::false_type{});
 
-    if (t0 < t1) {
-        uint32_t t = t0;
-        for (; t < full_end; ++t) tile(t, std::true_type{});
-        if (t < t1) tile(t, std::false_type{});
-    }
-
-    // lanes l and l + 32 hold two halves of the same row's ids
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) {
-        const float ov = __shfl_xor(best[g], 32);
-        const uint32_t oi = __shfl_xor(bidx[g], 32);
-        merge(best[g], bidx[g], ov, oi);
+        // lanes l and l + 32 hold two halves of the same row's ids
+        float bv = best[g];
+        uint32_t bi = bidx[g] == kNoIndex ? kNoIndex : bidx[g] + first_id;
+        const float ov = __shfl_xor(bv, 32);
+        const uint32_t oi = __shfl_xor(bi, 32);
+        merge(bv, bi, ov, oi);
         if (khalf == 0u && row_ok[g]) {
-            a.table[(uint64_t)row[g] * a.ranges + range] = make_key(best[g], bidx[g]);
+            a.table[(uint64_t)row[g] * a.ranges + range] = make_key(bv, bi);
         }
     }
 }
