@@ -77,6 +77,16 @@ struct GemmArgs {
     uint32_t row_wgs;      // workgroups per range (row groups / kWaves)
 };
 
+// The row of a 32-row group whose B operand (x) or A operand (w) lane l
+// carries.
+__device__ __forceinline__ uint32_t arow_x(uint32_t lane) { return lane & 31u; }
+
+// s_waitcnt lgkmcnt(0) with the other counters left alone.
+__device__ __forceinline__ void wait_lgkmcnt0()
+{
+    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
+}
+
 // Two fp32 values rounded to bf16 (round-to-nearest-even), packed lo | hi.
 __device__ __forceinline__ uint32_t round_pack2(float lo, float hi)
 {
@@ -124,12 +134,20 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
     static_assert(WPW * kWaves == TW || (TW < kWaves && WPW == 1 && kWaves % TW == 0),
                   "w copies split over waves");
     static_assert(BLOADS * 1024 == WROWS * kTileV * 2, "base copies cover the wave's rows");
-    // w tiles: row i (one id) at i * ROWB, its 16-byte chunk j at position
-    // j ^ (i & SWZ), so the 16 rows one matrix-operand read touches sit in 16
-    // different bank groups
-    __shared__ __attribute__((aligned(1024))) unsigned char w_lds[kRing][WBYTES];
-    // base of one full tile for each wave's rows
-    __shared__ __attribute__((aligned(16))) uint16_t base_lds[kRing][kWaves * WROWS * kTileV];
+    constexpr int BBYTES = kWaves * WROWS * kTileV * 2;  // one base tile, all waves
+    constexpr int XBYTES = 32 * R * 2;          // x of one 32-row group
+    static_assert(WBYTES + kWaves * XBYTES <= kRing * (WBYTES + BBYTES),
+                  "x staging fits beside w buffer 0");
+    // One LDS block: the w ring (kRing tiles; row i of a tile, one id, at
+    // i * ROWB, its 16-byte chunk j at position j ^ (i & SWZ), so the 16 rows
+    // one matrix-operand read touches sit in 16 different bank groups), then
+    // the base ring (one full tile for each wave's rows).  At start, the
+    // bytes past w buffer 0 hold each wave's x in turn (same swizzle).
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[kRing * (WBYTES + BBYTES)];
+    auto w_buf = [&](int buf) -> unsigned char* { return lds + buf * WBYTES; };
+    auto base_buf = [&](int buf) -> uint16_t* {
+        return reinterpret_cast<uint16_t*>(lds + kRing * WBYTES + buf * BBYTES);
+    };
 
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -174,7 +192,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
             uint32_t r = wrow0 + 16u * j + b_lrow;
             r = r < a.rows ? r : a.rows - 1u;
             dma16(a.base + (uint64_t)r * (uint64_t)a.stride_base + b_col + (uint64_t)t * kTileV,
-                  lds_addr(&base_lds[buf][(wave * WROWS + 16u * j) * kTileV]));
+                  lds_addr(base_buf(buf) + (wave * WROWS + 16u * j) * kTileV));
         }
     };
     // w: copy m of a tile fills LDS bytes [1024 m, 1024 m + 1024) with 64
@@ -191,7 +209,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
             uint32_t v = t * kTileV + i;
             v = v < a.V ? v : a.V - 1u;        // ids past V: any row, masked later
             dma16(a.w + (uint64_t)v * R + 8u * (p ^ (i & (uint32_t)SWZ)),
-                  lds_addr(reinterpret_cast<const uint16_t*>(&w_lds[buf][1024u * m])));
+                  lds_addr(reinterpret_cast<const uint16_t*>(w_buf(buf) + 1024u * m)));
         }
     };
 
@@ -217,27 +235,47 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
         issue_base(j);
         issue_w(j);
     };
-    issue(-2);
-
-    // B operands: the lane's draft rows of x, 8 of the 16 k of every step
+    // Prologue.  x is read into registers through LDS: each wave copies one
+    // 32-row group at a time (16-byte load-to-LDS, whole rows, so every copy
+    // reads contiguous memory; direct loads in the matrix layout would touch
+    // 32 rows per instruction and cost many more requests) into its own
+    // region past w buffer 0, then reads the B operands back.  w tile 0 is
+    // copied meanwhile; base tile 0 and tile 1 follow once every wave is
+    // done with its region, in the order the loop's wait counts assume.
+    issue_w(-2);
+    unsigned char* xstage = w_buf(1) + wave * XBYTES;
     bf16x8 bx[kGroups][KC];
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) {
+        // copy m: 64 chunks, row r = q / CPR of the group, position q % CPR
+        // holds logical chunk (q % CPR) ^ (r & SWZ), for q = 64 m + lane;
+        // rows past the last read the last row and never publish
+#pragma unroll
+        for (int m = 0; m < XBYTES / 1024; ++m) {
+            const uint32_t q = 64u * m + lane;
+            const uint32_t r = q / CPR;
+            const uint32_t p = q % CPR;
+            uint32_t srow = wrow0 + 32u * g + r;
+            srow = srow < a.rows ? srow : a.rows - 1u;
+            dma16(a.x + (uint64_t)srow * R + 8u * (p ^ (r & (uint32_t)SWZ)),
+                  lds_addr(reinterpret_cast<const uint16_t*>(xstage + 1024u * m)));
+        }
+        wait_vmcnt<0>();
+        const unsigned char* xrow = xstage + arow_x(lane) * ROWB;
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (row_ok[g]) {
-                v = *reinterpret_cast<const u32x4*>(a.x + (uint64_t)row[g] * R + 16 * c + 8 * khalf);
-            }
-            bx[g][c] = __builtin_bit_cast(bf16x8, v);
+            const uint32_t pos = (2u * c) ^ (khalf ^ (arow_x(lane) & (uint32_t)SWZ));
+            bx[g][c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xrow + 16u * pos));
         }
+        // the reads land before the region is copied over again
+        wait_lgkmcnt0();
     }
-    // Tile 0's copies and x have landed.  Waiting for all of it here also
-    // tells the compiler so; otherwise it cannot prove the conditional x
-    // loads complete and waits for every copy in flight before the first
-    // matrix instruction of each tile.
-    wait_vmcnt<0>();
+    __syncthreads();
+    issue_base(-2);
     issue(-1);
+    // base tile 0 has landed once only tile 1's copies remain (w tile 0
+    // landed with x)
+    wait_vmcnt_dyn(n_copies(-1));
 
     // Running first maximum of each of this lane's rows, ids held relative
     // to t0 * kTileV + 4 khalf (tile-uniform candidates, no per-lane id
@@ -267,7 +305,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
             for (int q = 0; q < 4; ++q) {
                 const uint32_t pc = (uint32_t)q ^ (lrow & 3u);
                 bv[q] = *reinterpret_cast<const u32x2*>(
-                    &base_lds[i % kRing][lrow * kTileV + pc * 8u + 4u * khalf]);
+                    base_buf(i % kRing) + lrow * kTileV + pc * 8u + 4u * khalf);
             }
         } else {
             const uint16_t* brow = a.base + (int64_t)(row_ok[g] ? row[g] : 0u) * a.stride_base;
@@ -308,7 +346,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
         } else {
             issue_base(i);
         }
-        const unsigned char* wrow = &w_lds[i % kRing][arow * ROWB];
+        const unsigned char* wrow = w_buf(i % kRing) + arow * ROWB;
         // logical chunk 2c + khalf of the lane's w row sits at position
         // (2c + khalf) ^ (row & SWZ)
         auto a_op = [&](int c) {
