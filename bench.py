@@ -44,6 +44,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 LLC_BYTES = 256 * 2 ** 20    # MI355X Infinity Cache
 SRC = os.path.join(ROOT, "vocab_wide_add_amd", "csrc", "xpress_argmax.hip")
+GEMM_SRC = os.path.join(ROOT, "vocab_wide_add_amd", "csrc", "readout_gemm.hip")
 
 
 def log(msg):
@@ -51,20 +52,20 @@ def log(msg):
     sys.stderr.flush()
 
 
-def source_digest() -> str:
-    with open(SRC, "rb") as f:
+def source_digest(src: str = SRC) -> str:
+    with open(src, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def traffic_for(workload: str):
+def traffic_for(workload: str, src: str = SRC):
     """HBM bytes per launch from committed PMC counter runs, if they were
-    taken on the current kernel source; else None."""
+    taken on the current source of the kernel (src); else None."""
     path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha256") != source_digest():
+    if t.get("kernel_source_sha256") != source_digest(src):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -349,7 +350,8 @@ def bench_gemm(args, np, torch, native, workloads):
               "input_sets": sets}
     out = result_line("readout with in-place bias (x @ w.T): effective GB/s and rows/s, "
                       "N=%d B=%d V=%d R=%d" % (w.N, w.B, w.V, w.R), name, config, w.bytes_read,
-                      w.rows, args.steps, args.warmup, wall, region_gpu, durs, 2, None)
+                      w.rows, args.steps, args.warmup, wall, region_gpu, durs, 2,
+                      traffic_for(name, GEMM_SRC))
     out["tflops"] = round(w.flops * args.steps / wall / 1e12, 2)
 
     # context: the unfused path -- a library matmul writing the bf16 bias,
