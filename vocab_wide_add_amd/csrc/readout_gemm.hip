@@ -213,11 +213,12 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
         }
     };
 
-    // Copy schedule: at the start of tile j every wave copies base tile j + 2
-    // (if full) and its share of w tile j + 2, two tiles ahead in a ring of
-    // three; the copies of tiles -2 and -1 go out before the loop.  n(j)
-    // counts the wave's copies at tile j; the wait at the end of tile j
-    // (everything but tile j's own copies) lands tile j + 1 for the barrier.
+    // Copy schedule: during tile j every wave copies base tile j + 2 (if
+    // full; at the start of the tile) and its share of w tile j + 2 (between
+    // the two row groups' epilogues), two tiles ahead in rings of three; the
+    // copies of tiles -2 and -1 go out before the loop.  n(j) counts the
+    // wave's copies during tile j, base before w; the wait at the end of tile
+    // j (everything but tile j's own copies) lands tile j + 1 for the barrier.
     auto n_copies = [&](int j) -> int {
         const int tt = j + 2;
         if (tt < 0 || tt >= T) return 0;
