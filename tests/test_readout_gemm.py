@@ -68,10 +68,12 @@ def _score(base, x, wt, r, v, V, R):
     return oracle.bf16_to_double(oracle.bf16_sum(int(base[r, v]), bias))
 
 
-def test_gemm_full_size_normal_within_derived_bound():
-    w = workloads.GEMM_WORKLOADS["gemm_normal_n32_b16_v152064_r256"]
+@pytest.mark.parametrize("name", ["gemm_normal_n32_b16_v152064_r256",
+                                  "gemm_normal_n1_b16_v152064_r256"])
+def test_gemm_full_size_normal_within_derived_bound(name):
+    w = workloads.GEMM_WORKLOADS[name]
     base, x, wt, blk0 = workloads.generate_gemm(w)
-    say("gemm full-size N(0,1)")
+    say("gemm full-size N(0,1) %s" % name)
     got = gpu_gemm(to_dev(base), to_dev(x), to_dev(wt), blk0, w.N, w.B, w.V, w.R, w.V)
     flat = got[:, 1:].reshape(-1)
     assert ((flat >= 0) & (flat < w.V)).all()
@@ -105,7 +107,9 @@ def _dyadic(rows, V, R, seed, pad=0):
 
 @pytest.mark.parametrize("R", [64, 128, 256])
 @pytest.mark.parametrize("N,B,V", [(1, 2, 1), (1, 2, 63), (1, 33, 64), (3, 12, 65),
-                                   (2, 17, 1000), (5, 21, 4097), (1, 2, 130)])
+                                   (2, 17, 1000), (5, 21, 4097), (1, 2, 130),
+                                   # the launch shape changes at 64 and 128 rows
+                                   (4, 17, 3000), (5, 14, 2999), (8, 17, 1001), (3, 44, 777)])
 def test_gemm_ragged_shapes(R, N, B, V):
     rows = N * (B - 1)
     pad = (-V) % 8 + (8 if V % 3 == 0 else 0)   # strides a multiple of 8, sometimes padded

@@ -59,9 +59,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTileV = 32;   // vocabulary ids per tile: one 32-id MFMA slice
-constexpr int kWaves = 8;    // waves per workgroup
+constexpr int kWavesMax = 8; // waves per workgroup above 128 rows (512 rows each)
 constexpr int kGroups = 2;   // 32-row groups per wave: they share every A operand read
-constexpr int kRing = 3;     // w tiles and base tiles resident in LDS
 constexpr int kAhead = 4;    // A-operand registers: reads run three steps ahead
 
 struct GemmArgs {
@@ -74,7 +73,7 @@ struct GemmArgs {
     uint32_t V;
     uint32_t tiles;        // ceil(V / kTileV)
     uint32_t ranges;       // vocabulary ranges (a multiple of 8)
-    uint32_t row_wgs;      // workgroups per range (row groups / kWaves)
+    uint32_t row_wgs;      // workgroups per range
 };
 
 // The row of a 32-row group whose B operand (x) or A operand (w) lane l
@@ -97,31 +96,31 @@ __device__ __forceinline__ uint32_t round_pack2(float lo, float hi)
 }
 
 // s_waitcnt vmcnt(n) for a wave-uniform n known only at run time (the
-// instruction takes an immediate); n above the largest case waits for all.
+// instruction takes an immediate): a chain of compares down from N; n above
+// N waits for all.
+template <int N>
 __device__ __forceinline__ void wait_vmcnt_dyn(int n)
 {
-    switch (n) {
-        case 14: wait_vmcnt<14>(); break;
-        case 13: wait_vmcnt<13>(); break;
-        case 12: wait_vmcnt<12>(); break;
-        case 11: wait_vmcnt<11>(); break;
-        case 10: wait_vmcnt<10>(); break;
-        case 9: wait_vmcnt<9>(); break;
-        case 8: wait_vmcnt<8>(); break;
-        case 7: wait_vmcnt<7>(); break;
-        case 6: wait_vmcnt<6>(); break;
-        case 5: wait_vmcnt<5>(); break;
-        case 4: wait_vmcnt<4>(); break;
-        case 3: wait_vmcnt<3>(); break;
-        case 2: wait_vmcnt<2>(); break;
-        case 1: wait_vmcnt<1>(); break;
-        default: wait_vmcnt<0>(); break;
+    if constexpr (N <= 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (n == N) {
+            wait_vmcnt<N>();
+        } else {
+            wait_vmcnt_dyn<N - 1>(n);
+        }
     }
 }
 
-template <int R>
-__global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
+// KW waves per workgroup (64 rows each): 8 with one workgroup per CU, or 1
+// or 2 (64 or 128 rows) with two per CU, so that few rows do not pay for 512.
+// RING tiles of w and base sit in LDS; copies run RING - 1 tiles ahead.
+template <int R, int KW, int RING>
+__global__ __launch_bounds__(KW * 64) void gemm_readout_kernel(GemmArgs a)
 {
+    constexpr int kWaves = KW;
+    constexpr int kRing = RING;
+    constexpr int AHEAD = RING - 1;
     constexpr int KC = R / 16;                  // MFMA steps over k
     constexpr int ROWB = R * 2;                 // bytes per w row in LDS
     constexpr int CPR = R / 8;                  // 16-byte chunks per w row
@@ -213,25 +212,28 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
         }
     };
 
-    // Copy schedule: during tile j every wave copies base tile j + 2 (if
-    // full; at the start of the tile) and its share of w tile j + 2 (between
-    // the two row groups' epilogues), two tiles ahead in rings of three; the
-    // copies of tiles -2 and -1 go out before the loop.  n(j) counts the
-    // wave's copies during tile j, base before w; the wait at the end of tile
-    // j (everything but tile j's own copies) lands tile j + 1 for the barrier.
+    // Copy schedule: during tile j every wave copies base tile j + AHEAD (if
+    // full; at the start of the tile) and its share of w tile j + AHEAD
+    // (between the two row groups' epilogues), into the ring buffer tile j - 1
+    // has just left; the copies of tiles 0 .. AHEAD - 1 go out before the
+    // loop.  n_copies(j) counts the wave's copies during tile j, base before
+    // w; the wait at the end of tile j (everything but the copies of the
+    // AHEAD - 1 latest tiles) lands tile j + 1 for the barrier.
     auto n_copies = [&](int j) -> int {
-        const int tt = j + 2;
+        const int tt = j + AHEAD;
         if (tt < 0 || tt >= T) return 0;
         return (tt < Tfull ? BLOADS : 0) + WPW;
     };
     auto issue_base = [&](int j) {
-        const int tt = j + 2;
+        const int tt = j + AHEAD;
         if (tt >= 0 && tt < Tfull) dma_base(t0 + (uint32_t)tt, tt % kRing);
     };
     auto issue_w = [&](int j) {
-        const int tt = j + 2;
+        const int tt = j + AHEAD;
         if (tt >= 0 && tt < T) dma_w(t0 + (uint32_t)tt, tt % kRing);
     };
+    constexpr int kMaxCount = (AHEAD - 1) * (BLOADS + WPW);
+    static_assert(kMaxCount < 64, "wait counts fit vmcnt");
     auto issue = [&](int j) {
         issue_base(j);
         issue_w(j);
@@ -241,13 +243,18 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
     // reads contiguous memory; direct loads in the matrix layout would touch
     // 32 rows per instruction and cost many more requests) into its own
     // region past w buffer 0, then reads the B operands back.  w tile 0 is
-    // copied meanwhile; base tile 0 and tile 1 follow once every wave is
-    // done with its region, in the order the loop's wait counts assume.
-    issue_w(-2);
+    // copied meanwhile; base tile 0 and tiles 1 .. AHEAD - 1 follow once
+    // every wave is done with its region, in the order the loop's wait
+    // counts assume.
+    issue_w(-AHEAD);
     unsigned char* xstage = w_buf(1) + wave * XBYTES;
+    // a wave whose second row group lies wholly past the last row skips it
+    // (wave-uniform), here and in every tile
+    const bool g1 = wrow0 + 32u < a.rows;
     bf16x8 bx[kGroups][KC];
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) {
+        if (g == 1 && !g1) break;
         // copy m: 64 chunks, row r = q / CPR of the group, position q % CPR
         // holds logical chunk (q % CPR) ^ (r & SWZ), for q = 64 m + lane;
         // rows past the last read the last row and never publish
@@ -272,11 +279,15 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
         wait_lgkmcnt0();
     }
     __syncthreads();
-    issue_base(-2);
-    issue(-1);
-    // base tile 0 has landed once only tile 1's copies remain (w tile 0
-    // landed with x)
-    wait_vmcnt_dyn(n_copies(-1));
+    issue_base(-AHEAD);
+    int later = 0;
+    for (int j = 1 - AHEAD; j < 0; ++j) {
+        issue(j);
+        later += n_copies(j);
+    }
+    // base tile 0 has landed once only the later tiles' copies remain (w
+    // tile 0 landed with x)
+    wait_vmcnt_dyn<kMaxCount>(later);
 
     // Running first maximum of each of this lane's rows, ids held relative
     // to t0 * kTileV + 4 khalf (tile-uniform candidates, no per-lane id
@@ -334,16 +345,17 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
     // from different waves slow each other down.  Full tiles run in the loop;
     // a ragged last tile runs after it, where x is no longer live, so its
     // clamped loads do not compete with x for registers.
-    auto step = [&](int i, auto full_tag, auto steady_tag) {
+    auto step = [&](int i, auto full_tag, auto steady_tag, auto ng_tag) {
         constexpr bool FULL = decltype(full_tag)::value;
-        // steady: tile i + 2 exists and is full, so the copies and the wait
-        // count are the fixed ones and the body has no branches
+        constexpr int NG = decltype(ng_tag)::value;  // row groups in use
+        // steady: tile i + AHEAD exists and is full, so the copies and the
+        // wait count are the fixed ones and the body has no branches
         constexpr bool STEADY = decltype(steady_tag)::value;
         const uint32_t tv = (t0 + (uint32_t)i) * kTileV;
         // base copies now, w copies between the two groups' epilogues: each
         // wave's copies go to the address unit in two smaller bursts
         if constexpr (STEADY) {
-            dma_base(t0 + (uint32_t)(i + 2), (i + 2) % kRing);
+            dma_base(t0 + (uint32_t)(i + AHEAD), (i + AHEAD) % kRing);
         } else {
             issue_base(i);
         }
@@ -358,7 +370,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
         // feeds both row groups' matrix instructions; a scheduling barrier
         // after each step keeps that order.
 #pragma unroll
-        for (int g = 0; g < kGroups; ++g) acc[g] = f32x16{};
+        for (int g = 0; g < NG; ++g) acc[g] = f32x16{};
         bf16x8 ar[kAhead];
 #pragma unroll
         for (int c = 0; c < kAhead - 1 && c < KC; ++c) ar[c] = a_op(c);
@@ -366,7 +378,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
         for (int c = 0; c < KC; ++c) {
             if (c + kAhead - 1 < KC) ar[(c + kAhead - 1) % kAhead] = a_op(c + kAhead - 1);
 #pragma unroll
-            for (int g = 0; g < kGroups; ++g) {
+            for (int g = 0; g < NG; ++g) {
                 acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[c % kAhead], bx[g][c], acc[g],
                                                                  0, 0, 0);
             }
@@ -376,16 +388,21 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
         // work is not spread between them (on this part vector and matrix
         // instructions interleaved in one wave slow each other beyond a few
         // per step).
-        asm volatile("" : "+v"(acc[0]), "+v"(acc[1]));
+        if constexpr (NG == 2) {
+            asm volatile("" : "+v"(acc[0]), "+v"(acc[1]));
+        } else {
+            asm volatile("" : "+v"(acc[0]));
+        }
 #pragma unroll
         for (int g = 0; g < kGroups; ++g) {
             if (g == 1) {
                 if constexpr (STEADY) {
-                    dma_w(t0 + (uint32_t)(i + 2), (i + 2) % kRing);
+                    dma_w(t0 + (uint32_t)(i + AHEAD), (i + AHEAD) % kRing);
                 } else {
                     issue_w(i);
                 }
             }
+            if (g >= NG) break;
             u32x2 bv[4];
             load_bv(g, i, tv, full_tag, bv);
 #pragma unroll
@@ -406,18 +423,31 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
                 }
             }
         }
-        // tile i + 1 went out at tile i - 1; only tile i's copies may remain
+        // tile i + 1 went out during tile i + 1 - AHEAD; only the copies of
+        // the tiles after that may remain
         if constexpr (STEADY) {
-            wait_vmcnt<BLOADS + WPW>();
+            wait_vmcnt<kMaxCount>();
         } else {
-            if (i + 1 < T) wait_vmcnt_dyn(n_copies(i));
+            if (i + 1 < T) {
+                int later = 0;
+                for (int j = i + 2 - AHEAD; j <= i; ++j) later += n_copies(j);
+                wait_vmcnt_dyn<kMaxCount>(later);
+            }
         }
         __syncthreads();
     };
-    int i = 0;
-    for (; i + 2 < Tfull; ++i) step(i, std::true_type{}, std::true_type{});
-    for (; i < Tfull; ++i) step(i, std::true_type{}, std::false_type{});
-    if (Tfull < T) step(T - 1, std::false_type{}, std::false_type{});
+    auto run = [&](auto ng_tag) {
+        int i = 0;
+        for (; i + AHEAD < Tfull; ++i) step(i, std::true_type{}, std::true_type{}, ng_tag);
+        for (; i < Tfull; ++i) step(i, std::true_type{}, std::false_type{}, ng_tag);
+        if (Tfull < T) step(T - 1, std::false_type{}, std::false_type{}, ng_tag);
+    };
+    // both paths pass the same barriers, one per tile
+    if (g1) {
+        run(std::integral_constant<int, 2>{});
+    } else {
+        run(std::integral_constant<int, 1>{});
+    }
 
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) {
@@ -434,9 +464,19 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_readout_kernel(GemmArgs a)
 }
 
 template <int R>
-hipError_t launch_gemm(const GemmArgs& a, uint32_t grid, hipStream_t stream)
+hipError_t launch_gemm(const GemmArgs& a, int waves, uint32_t grid, hipStream_t stream)
 {
-    hipLaunchKernelGGL(gemm_readout_kernel<R>, dim3(grid), dim3(kWaves * 64), 0, stream, a);
+    // one wave: a ring of four (60 to 80 KiB at R = 256, two workgroups per
+    // CU) so copies run three tiles ahead of a wave that computes a tile in a
+    // fraction of the memory latency; otherwise three
+    switch (waves) {
+        case 1: hipLaunchKernelGGL((gemm_readout_kernel<R, 1, 4>), dim3(grid), dim3(64), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((gemm_readout_kernel<R, 2, 3>), dim3(grid), dim3(128), 0, stream, a); break;
+        default:
+            hipLaunchKernelGGL((gemm_readout_kernel<R, kWavesMax, 3>), dim3(grid), dim3(kWavesMax * 64),
+                               0, stream, a);
+            break;
+    }
     return hipGetLastError();
 }
 
@@ -475,11 +515,15 @@ extern "C" int xpress_readout_gemm_argmax_to_blk(const uint16_t* base, const uin
     a.rows = (uint32_t)rows;
     a.V = (uint32_t)V;
     a.tiles = (uint32_t)((V + kTileV - 1) / kTileV);
-    const int64_t groups = (rows + 31) / 32;
-    a.row_wgs = (uint32_t)((groups + kWaves * kGroups - 1) / (kWaves * kGroups));
-    // about one workgroup per CU (a workgroup fills its CU's LDS and two
-    // waves per SIMD); ranges a multiple of 8 (one per XCD slot)
-    int64_t ranges = (int64_t)device_cus() / a.row_wgs;
+    // Up to 64 rows: one wave per workgroup, up to 128: two (two workgroups
+    // per CU either way, LDS allowing); beyond: eight waves (512 rows), one
+    // workgroup per CU, and as many workgroups per range as the rows need.
+    const int waves = rows <= 64 ? 1 : rows <= 128 ? 2 : kWavesMax;
+    const int per_cu = waves == kWavesMax ? 1 : 2;
+    const int64_t rows_per_wg = (int64_t)waves * 32 * kGroups;
+    a.row_wgs = (uint32_t)((rows + rows_per_wg - 1) / rows_per_wg);
+    // ranges a multiple of 8 (one per XCD slot)
+    int64_t ranges = (int64_t)device_cus() * per_cu / a.row_wgs;
     ranges = ranges / 8 * 8;
     if (ranges < 8) ranges = 8;
     const int64_t max_ranges = ((int64_t)a.tiles + 7) / 8 * 8;
@@ -493,9 +537,9 @@ extern "C" int xpress_readout_gemm_argmax_to_blk(const uint16_t* base, const uin
     const uint32_t grid = a.row_wgs * a.ranges;
     hipError_t e;
     switch (R) {
-        case 64: e = launch_gemm<64>(a, grid, stream); break;
-        case 128: e = launch_gemm<128>(a, grid, stream); break;
-        default: e = launch_gemm<256>(a, grid, stream); break;
+        case 64: e = launch_gemm<64>(a, waves, grid, stream); break;
+        case 128: e = launch_gemm<128>(a, waves, grid, stream); break;
+        default: e = launch_gemm<256>(a, waves, grid, stream); break;
     }
     if (e != hipSuccess) return hip_fail(e);
     e = launch_reduce_table(a.table, blk, nullptr, a.rows, (uint32_t)(B - 1), a.V, a.ranges,

@@ -285,6 +285,7 @@ GEMM_WORKLOADS = {
         GemmWorkload("gemm_small_n8_b8_v32000_r256", 8, 8, 32000, 256, 21, True),
         GemmWorkload("gemm_dyadic_n32_b16_v152064_r256", 32, 16, 152064, 256, 22, True),
         GemmWorkload("gemm_normal_n32_b16_v152064_r256", 32, 16, 152064, 256, 23, False),
+        GemmWorkload("gemm_normal_n1_b16_v152064_r256", 1, 16, 152064, 256, 24, False),
     ]
 }
 
