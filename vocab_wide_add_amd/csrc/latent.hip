@@ -637,10 +637,33 @@ __global__ void __launch_bounds__(kThreads) latent_mix_staged(MixArgs a)
     const uint32_t nb = (a.N - n0 < a.bpt) ? (a.N - n0) : a.bpt;
     const uint32_t rows = nb * B;
 
-    // every load here is older than the chunk loads the contraction counts
+    // Every load here goes out at once, older than the chunk loads the
+    // contraction counts: the token ids (they gate the embedding copies),
+    // the mixer slice and the cache rows.  The slice is stored to LDS before
+    // any chunk copy is issued, so the wait for it covers these loads only
+    // (a load-then-store loop would pay one memory latency per pass).
+    constexpr int kN = DmaRows<kSlabRows>::kN;
+    int64_t tok[kN];
+#pragma unroll
+    for (int j = 0; j < kN; ++j) {
+        const uint32_t i = 32 * j + 8 * wave + (lane >> 3);
+        const uint32_t ic = i < rows ? i : 0;
+        const uint32_t n = n0 + ic / B, slot = ic % B;
+        const int64_t* tp = (slot == 0) ? a.am1 + n : a.blk + (size_t)n * B + slot - 1;
+        tok[j] = *tp;
+    }
+    constexpr int kMixPer = kMaxB * kMaxB * 4 / kThreads;
+    static_assert(kMixPer * kThreads == kMaxB * kMaxB * 4, "mixer slice split over threads");
     const uint32_t mix_chunks = B * B * 4;
-    for (uint32_t q = tid; q < mix_chunks; q += kThreads) {
-        mixs_dyn[q] = load16(a.mixl + (size_t)(q >> 2) * R + c0 + 8 * (q & 3));
+    // unconditional loads (chunks past the slice repeat its last one and are
+    // not stored): a predicated load with a default value makes the compiler
+    // wait for it on the spot
+    u32x4 mreg[kMixPer];
+#pragma unroll
+    for (int q = 0; q < kMixPer; ++q) {
+        uint32_t c = tid + q * kThreads;
+        c = c < mix_chunks ? c : mix_chunks - 1u;
+        mreg[q] = load16(a.mixl + (size_t)(c >> 2) * R + c0 + 8 * (c & 3));
     }
     float xh[16];
 #pragma unroll
@@ -648,19 +671,21 @@ __global__ void __launch_bounds__(kThreads) latent_mix_staged(MixArgs a)
         const uint32_t i = kTile * wave + acc_row(r, lane);
         xh[r] = from_bf16(a.xh[((size_t)n0 * B + (i < rows ? i : 0)) * R + c0 + (lane & 31)]);
     }
-    const uint16_t* abase[DmaRows<kSlabRows>::kN];
+    const uint16_t* abase[kN];
     uint32_t zero_row = 0;
 #pragma unroll
-    for (int j = 0; j < DmaRows<kSlabRows>::kN; ++j) {
+    for (int j = 0; j < kN; ++j) {
         const uint32_t i = 32 * j + 8 * wave + (lane >> 3);
-        const uint32_t ic = i < rows ? i : 0;
-        const uint32_t n = n0 + ic / B, slot = ic % B;
-        const int64_t tok = (slot == 0) ? a.am1[n] : a.blk[(size_t)n * B + slot - 1];
-        const bool ok = tok >= 0 && tok < a.V;
-        abase[j] = a.w1 + (size_t)(ok ? tok : 0) * R;
+        const bool ok = tok[j] >= 0 && tok[j] < a.V;
+        abase[j] = a.w1 + (size_t)(ok ? tok[j] : 0) * R;
         // an id outside [0, V) reads as a zero embedding row (padding rows
         // beyond the tile's blocks are never read back)
         if (i < rows && !ok) zero_row |= 1u << j;
+    }
+#pragma unroll
+    for (int q = 0; q < kMixPer; ++q) {
+        const uint32_t c = tid + q * kThreads;
+        if (c < mix_chunks) mixs_dyn[c] = mreg[q];
     }
     const uint16_t* bbase[1] = {a.wlat + (size_t)(c0 + 8 * wave + (lane >> 3)) * R};
     DmaRows<kSlabRows> da;
