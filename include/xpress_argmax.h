@@ -140,7 +140,11 @@ int xpress_topc_argmax_to_blk(const uint16_t* base_c, const uint16_t* bias_c,
  * accumulation order is the matrix cores'; where every partial sum of the
  * dot products is exact (e.g. inputs on a coarse dyadic grid) the result is
  * bit-identical to rounding the exact dot product.  Asynchronous; two
- * launches; uses the (device, stream) workspace (rows x ranges keys).
+ * launches; uses the (device, stream) workspace (rows x ranges keys, at most
+ * rows x 512 x 8 bytes), grown on first use.  xpress_reserve does not size
+ * it: before capturing this call into a HIP graph, make one call with at
+ * least as many rows on the same stream outside capture (a capture that
+ * would have to grow it returns XPRESS_ECAPTURE).
  */
 int xpress_readout_gemm_argmax_to_blk(const uint16_t* base, const uint16_t* x,
                                       const uint16_t* w, int64_t* blk, int64_t N,

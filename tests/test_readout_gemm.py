@@ -157,3 +157,44 @@ def test_gemm_invalid_arguments_raise():
         native.xpress_readout_gemm_argmax_to_blk(b, b, b, blk, 1, 2, 8, 96, 8)
     with pytest.raises(native.XpressError):   # misaligned x
         native.xpress_readout_gemm_argmax_to_blk(b, b.data_ptr() + 2, b, blk, 1, 2, 8, 64, 8)
+
+
+@pytest.mark.parametrize("N,B,V,R", [(2, 8, 5000, 128),     # 14 rows: one wave per workgroup
+                                     (12, 11, 3000, 64),    # 120 rows: two waves
+                                     (10, 17, 2000, 256)])  # 160 rows: eight waves
+def test_gemm_graph_replay_matches_eager(N, B, V, R):
+    """One call outside capture sizes the (device, stream) workspace; the call
+    captured into a HIP graph then replays on fresh inputs copied in between,
+    each replay checked against an eager call and the oracle."""
+    import torch
+    rows = N * (B - 1)
+    cases = [_dyadic(rows, V, R, seed=700 + k) for k in range(3)]
+    blk0 = np.full((N, B), -1, dtype=np.int64)
+    blk0[:, 0] = 5
+    base_d, x_d, w_d = (to_dev(a) for a in cases[0])
+    blk_d = to_dev(blk0)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    native.xpress_readout_gemm_argmax_to_blk(base_d, x_d, w_d, blk_d, N, B, V, R, V, stream=s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    say("gemm graph capture N=%d B=%d V=%d R=%d" % (N, B, V, R))
+    with torch.cuda.graph(g, stream=s):
+        native.xpress_readout_gemm_argmax_to_blk(base_d, x_d, w_d, blk_d, N, B, V, R, V, stream=s)
+    for rep in range(6):
+        base, x, wt = cases[rep % 3]
+        base_d.copy_(to_dev(base))
+        x_d.copy_(to_dev(x))
+        w_d.copy_(to_dev(wt))
+        blk_d.copy_(to_dev(blk0))
+        torch.cuda.synchronize()
+        say("gemm graph replay %d" % rep)
+        g.replay()
+        torch.cuda.synchronize()
+        got = blk_d.cpu().numpy()
+        eager = gpu_gemm(base_d, x_d, w_d, blk0, N, B, V, R, V)
+        assert np.array_equal(got, eager), rep
+        want = blk0.copy()
+        want[:, 1:] = oracle.gemm_argmax_rows(base, x, wt, range(rows), V, R, V,
+                                              threads=ORACLE_THREADS).reshape(N, B - 1)
+        assert np.array_equal(got, want), rep
