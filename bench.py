@@ -347,7 +347,7 @@ def bench_gemm(args, np, torch, native, workloads):
     got = dev[last_set(args, sets)][3].cpu().numpy()[:, 1:].reshape(-1)
     config = {"workload": name, "op": "readout_gemm", "N": w.N, "B": w.B, "V": w.V, "R": w.R,
               "rows": w.rows, "bytes_per_step": w.bytes_read, "flops_per_step": w.flops,
-              "input_sets": sets}
+              "input_sets": sets, "launches_per_step": 2}
     out = result_line("readout with in-place bias (x @ w.T): effective GB/s and rows/s, "
                       "N=%d B=%d V=%d R=%d" % (w.N, w.B, w.V, w.R), name, config, w.bytes_read,
                       w.rows, args.steps, args.warmup, wall, region_gpu, durs, 2,

@@ -225,6 +225,37 @@ def test_equal_maxima_across_workgroups(combine, splits):
     assert np.array_equal(want, oracle_blk(base, bias, blk0, N, B, V, V, V))
 
 
+@pytest.mark.parametrize("splits", [65, 200, 513, 1100])
+def test_two_pass_many_splits(splits):
+    """More keys per row than one wave holds, which the second pass loads in
+    batches of 512: equal maxima planted at the starts of two splits, on
+    either side of key 64 and key 512, must still give the lowest index."""
+    V = 40000
+    nvec = V // 8
+    N, B = 4, 4
+    rows = N * (B - 1)
+    rng = np.random.default_rng(900 + splits)
+    base = workloads.f32_to_bf16_bits(rng.normal(0.0, 4.0, (rows, V)).astype(np.float32))
+    bias = workloads.f32_to_bf16_bits(rng.normal(0.0, 0.5, (rows, V)).astype(np.float32))
+    marks = sorted({s for s in (0, 1, 63, 64, 65, 511, 512, 513, splits - 1) if s < splits})
+    start = lambda s: (s * nvec // splits) * 8
+    want = np.full((N, B), -3, dtype=np.int64)
+    blk0 = want.copy()
+    for r in range(rows):
+        s1 = marks[r % len(marks)]
+        s2 = marks[(r * 5 + 3) % len(marks)]
+        s1, s2 = min(s1, s2), max(s1, s2)
+        for s in {s1, s2}:
+            base[r, start(s)] = 0x4220   # 40.0: above every Gaussian sum here
+            bias[r, start(s)] = 0x0000
+        want[r // (B - 1), 1 + r % (B - 1)] = start(s1)
+    assert np.array_equal(want, oracle_blk(base, bias, blk0, N, B, V, V, V))
+    say("two-pass many splits=%d" % splits)
+    with Plan(native.XPRESS_COMBINE_TWO_PASS, splits, 64):
+        got = gpu_blk(to_dev(base), to_dev(bias), blk0, N, B, V, V, V)
+    assert np.array_equal(got, want)
+
+
 @pytest.mark.parametrize("combine", COMBINES)
 def test_signed_zero_and_special_rows(combine):
     """-0 before +0 in another workgroup, all -inf rows, +inf ties, subnormal

@@ -370,20 +370,43 @@ __global__ __launch_bounds__(256) void topc_wave_kernel(const uint16_t* __restri
     }
 }
 
+// Keys a lane of the second pass loads before comparing any.
+constexpr int kReduceBatch = 8;
+
 // Second pass of the two-pass combine: one wave per row reads the row's
 // `splits` keys with consecutive lanes on consecutive keys, keeps the largest
 // (a larger key is a larger value or, on equal values, a smaller index),
-// reduces over the wave and writes blk from lane 0.
+// reduces over the wave and writes blk from lane 0.  Loads are unconditional
+// (clamped to the row's last key) and masked afterwards, so that a batch of
+// them is in flight together: a predicated load would be waited on alone.
 __global__ __launch_bounds__(256) void reduce_keys_kernel(RowArgs a)
 {
     const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t last = a.splits - 1u;
     for (uint32_t row = blockIdx.x * 4u + (threadIdx.x >> 6); row < a.rows;
          row += gridDim.x * 4u) {
         const uint64_t* k = a.keys + (uint64_t)row * a.splits;
         unsigned long long best = 0;
-        for (uint32_t s = lane; s < a.splits; s += 64u) {
-            const unsigned long long v = k[s];
-            best = v > best ? v : best;
+        if (a.splits <= 64u) {
+            // at most one key per lane
+            const unsigned long long v = k[lane < a.splits ? lane : last];
+            best = lane < a.splits ? v : 0ull;
+        } else {
+            // batches of up to 64 * kReduceBatch keys: one memory latency per
+            // batch rather than one per 64 keys
+            for (uint32_t s0 = 0; s0 < a.splits; s0 += 64u * kReduceBatch) {
+                unsigned long long v[kReduceBatch];
+#pragma unroll
+                for (int u = 0; u < kReduceBatch; ++u) {
+                    const uint32_t s = s0 + 64u * u + lane;
+                    v[u] = k[s < a.splits ? s : last];
+                }
+#pragma unroll
+                for (int u = 0; u < kReduceBatch; ++u) {
+                    const bool in = s0 + 64u * u + lane < a.splits;
+                    best = in && v[u] > best ? v[u] : best;
+                }
+            }
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) {
