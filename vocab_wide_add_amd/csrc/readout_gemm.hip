@@ -405,6 +405,14 @@ __global__ __launch_bounds__(KW * 64) void gemm_readout_kernel(GemmArgs a)
             if (g >= NG) break;
             u32x2 bv[4];
             load_bv(g, i, tv, full_tag, bv);
+            // Within the tile a candidate's id is its position in the tile,
+            // an immediate operand of the select (a wave-uniform id would
+            // have to be copied into a vector register for every candidate:
+            // a select reads at most one scalar operand, and the condition
+            // is one); the running id is held relative to the tile meanwhile
+            // (wrapping arithmetic) and restored after the tile.
+            float tb = best[g];
+            uint32_t tp = bidx[g] - (uint32_t)(kTileV * i);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const uint32_t s01 =
@@ -416,12 +424,14 @@ __global__ __launch_bounds__(KW * 64) void gemm_readout_kernel(GemmArgs a)
                 for (int jj = 0; jj < 4; ++jj) {
                     // ids past V exist only in a ragged last tile
                     const bool take =
-                        FULL ? (sv[jj] > best[g])
-                             : ((tv + 8u * q + 4u * khalf + jj < a.V) && (sv[jj] > best[g]));
-                    best[g] = take ? sv[jj] : best[g];
-                    bidx[g] = take ? (uint32_t)(kTileV * i + 8 * q + jj) : bidx[g];
+                        FULL ? (sv[jj] > tb)
+                             : ((tv + 8u * q + 4u * khalf + jj < a.V) && (sv[jj] > tb));
+                    tb = take ? sv[jj] : tb;
+                    tp = take ? (uint32_t)(8 * q + jj) : tp;
                 }
             }
+            best[g] = tb;
+            bidx[g] = tp + (uint32_t)(kTileV * i);
         }
         // tile i + 1 went out during tile i + 1 - AHEAD; only the copies of
         // the tiles after that may remain
