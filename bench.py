@@ -34,6 +34,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -53,8 +54,14 @@ def log(msg):
 
 
 def source_digest(src: str = SRC) -> str:
-    with open(src, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """SHA-256 of a kernel source's code: comments removed and whitespace runs
+    collapsed, so that counters recorded for the code stay valid across edits
+    of its comments and are dropped by any change to the code itself."""
+    with open(src, encoding="utf-8") as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
 
 
 def traffic_for(workload: str, src: str = SRC):

@@ -22,11 +22,12 @@
 //   * a wave owns 64 draft rows (two 32-row groups whose matrix instructions
 //     share every A-operand read); their x rows stay in registers as the B
 //     operands for the whole launch;
-//   * a workgroup of 8 waves covers 512 rows and a contiguous range of
-//     32-id tiles; w tiles and each wave's base tiles are copied straight
-//     into LDS by the 16-byte load-to-LDS instruction, two tiles ahead in
-//     rings of three, and each wave waits only on its own copies (explicit
-//     counts) before the one barrier per tile;
+//   * a workgroup of 8 waves covers 512 rows (above 128 rows; 2 waves up to
+//     128 rows, 1 wave up to 64) and a contiguous range of 32-id tiles; w
+//     tiles and each wave's base tiles are copied straight into LDS by the
+//     16-byte load-to-LDS instruction, two tiles ahead in rings of three
+//     (three ahead in a ring of four for one wave), and each wave waits only
+//     on its own copies (explicit counts) before the one barrier per tile;
 //   * all waves run the same phase together (matrix instructions, then the
 //     epilogue): measured on this part, a SIMD's two waves retire matrix
 //     instructions faster together than one alone, and vector instructions

@@ -24,10 +24,12 @@
 //     merged in (value desc, index asc) order, which is the total order whose
 //     maximum is the first maximum;
 //   * the workgroups of a row meet in one of three ways (see
-//     xpress_set_plan in the header): a single workgroup per row, a packed
-//     64-bit key folded with an agent-scope atomic max plus an arrival count
-//     whose last arriver writes blk and clears the slot, or a key table plus
-//     a second small kernel.
+//     xpress_set_plan in the header): a single workgroup per row; one
+//     64-bit word per row holding the best packed key and an arrival count,
+//     updated by agent-scope compare-and-swap, whose last arriver writes blk
+//     and clears the word; or a key table plus a second small kernel.  The
+//     balanced plan cuts the flattened rows into equal ranges and folds the
+//     rows it splits through the same compare-and-swap word.
 // The pages' own design (a [rows, chunks] fp32 + int64 scratch and a second
 // kernel per row) is the two-pass variant here, with one u64 key per chunk.
 
@@ -499,12 +501,13 @@ Plan make_plan(const uint16_t* base, const uint16_t* bias, int64_t rows, int64_t
         ot = g_override_threads;
     }
     p.threads = ot ? ot : auto_threads(rows, V, p.vec);
-    // Measured on MI355X: one workgroup per row streams at the same rate as
-    // a plain read kernel once there are a few hundred rows, and stays the
+    // Measured on MI355X: one workgroup per row streams within ~3% of a
+    // plain read kernel once there are a few hundred rows, and stays the
     // fastest down to tens of rows (the second launch of the two-pass
-    // combine costs ~2 us; the atomic combine's release fence costs ~40 ns
-    // per workgroup, serialised).  Only a handful of very wide rows leave
-    // most CUs idle; those are split and combined in two passes.
+    // combine costs ~2 us; the compare-and-swap folds of the atomic combine
+    // queue up on each row's word: 47.8 us with 2 splits and 70.4 us with 8
+    // at 480 x 152064, against 44.8 us unsplit).  Only a handful of very wide
+    // rows leave most CUs idle; those are split and combined in two passes.
     const int64_t per_split = (int64_t)p.threads * kUnroll * 2 * (p.vec ? 8 : 1);
     int64_t max_splits = V / per_split;
     if (max_splits < 1) max_splits = 1;
