@@ -17,15 +17,23 @@
 // a latency chain through a single CU.  Here the stage is three MFMA kernels
 // in stream order, each spreading its weight slice over many workgroups:
 //
-//   mix   per (32 x-rows, 32 channels): the gathered embeddings times W_lat on
-//         v_mfma_f32_32x32x16_bf16 with K split over 4 waves, the partials
-//         summed in LDS with the hidden cache, then the folded mixer per
-//         channel from an LDS copy of its slice of mixl.  Writes u (fp32) and
-//         bf16(u) for the slots that are read out.
-//   gate  per (32 rows, 32 hidden units): bf16(u) times wg and wu, K split
-//         over 4 waves; m = bf16(silu(g) * v).
-//   down  per (32 rows, 32 channels): m times wd, K split over 4 waves, plus
-//         the residual u, rounded to bf16 into the output.
+//   mix   per (whole blocks of x-rows, 32 channels): the gathered embeddings
+//         times W_lat on v_mfma_f32_32x32x16_bf16, summed with the hidden
+//         cache in LDS, then the folded mixer per channel from an LDS copy of
+//         its slice of mixl.  Writes u (fp32) and bf16(u) for the slots that
+//         are read out.
+//   gate  per (rows, 32 hidden units): bf16(u) times wg and wu;
+//         m = bf16(silu(g) * v).
+//   down  per (rows, 32 channels): m times wd plus the residual u, rounded
+//         to bf16 into the output.
+//
+// Each kernel comes in two shapes.  The direct kernels give a workgroup's
+// four waves 32 * slabs rows and split the contraction over 4 / slabs waves
+// (slabs = 1, 2 or 4; partial sums meet in LDS), loading operands straight
+// into registers: the most slabs that still give every compute unit a
+// workgroup.  From 2048 rows on, the staged kernels take 128 rows per
+// workgroup (one 32-row slab per wave) and copy the operands into LDS in
+// coalesced 64-wide contraction chunks, one chunk ahead.
 //
 // The kernel boundaries are the cross-workgroup syncs: u and m go through a
 // small workspace (L2 / MALL resident).  Each grid is 1-D with the weight
