@@ -125,6 +125,26 @@ def test_gemm_ragged_shapes(R, N, B, V):
     assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("N,B,V,R", [(37, 15, 1001, 64),    # 518 rows: 2 workgroups per range, 6 rows in the second
+                                     (40, 16, 3000, 256),   # 600 rows
+                                     (70, 16, 2000, 128)])  # 1050 rows: 3 workgroups per range
+def test_gemm_several_workgroups_per_range(N, B, V, R):
+    """Above 512 rows each vocabulary range is covered by several 512-row
+    workgroups placed on one XCD; the last one is partly empty."""
+    rows = N * (B - 1)
+    pad = (-V) % 8
+    S = V + pad
+    base, x, wt = _dyadic(rows, V, R, seed=rows + V + R, pad=pad)
+    blk0 = np.full((N, B), -1, dtype=np.int64)
+    blk0[:, 0] = 11
+    want = blk0.copy()
+    want[:, 1:] = oracle.gemm_argmax_rows(base, x, wt, range(rows), V, R, S,
+                                          threads=ORACLE_THREADS).reshape(N, B - 1)
+    say("gemm several workgroups per range N=%d B=%d V=%d R=%d" % (N, B, V, R))
+    got = gpu_gemm(to_dev(base), to_dev(x), to_dev(wt), blk0, N, B, V, R, S)
+    assert np.array_equal(got, want)
+
+
 def test_gemm_repeated_calls_and_guard_cells():
     import torch
     N, B, V, R = 4, 16, 20000, 128
