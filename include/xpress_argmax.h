@@ -230,7 +230,7 @@ int xpress_latent_reserve(int64_t N, int64_t B, int64_t R, int64_t H, hipStream_
  * 32-row slab over the whole contraction, slabs = 2 or 1 split the
  * contraction over 2 or 4 waves and sum the partials in LDS; 8 selects the
  * LDS-staged kernels (128 rows per workgroup, operands copied to LDS in
- * coalesced 64-wide contraction chunks, one chunk ahead).  Arguments are the
+ * coalesced 64-wide contraction chunks, up to four in flight).  Arguments are the
  * choices for the mix, gate and down kernels: 1, 2, 4 or 8, or 0 for the
  * library's choice per shape (staged from 2048 rows on, else the most slabs
  * that still give each compute unit a workgroup).  Results are identical up
