@@ -494,13 +494,82 @@ def bench_latent(args, np, torch, native, workloads):
     return out
 
 
+def bench_pass(args, np, torch, native, workloads):
+    """One whole pass: the latent stage (reading blk) feeding the readout
+    with in-place bias (writing blk in place), back to back on one stream."""
+    name = args.workload if (args.workload or "").startswith("pass_") else \
+        workloads.PASS_BENCH_WORKLOAD
+    lname, gname = workloads.PASS_WORKLOADS[name]
+    lw, gw = workloads.LATENT_WORKLOADS[lname], workloads.GEMM_WORKLOADS[gname]
+    assert (lw.N, lw.B, lw.R, lw.V) == (gw.N, gw.B, gw.R, gw.V)
+    N, B, R, H, V = lw.N, lw.B, lw.R, lw.H, lw.V
+    log("generating %s (%s + %s)" % (name, lname, gname))
+    d = workloads.generate_latent(lw)
+    base, _, wt, _ = workloads.generate_gemm(gw)
+    keys = ("blk", "am1", "xh", "w1", "wlat", "mixl", "wg", "wu", "wd")
+    dev = {k: torch.from_numpy(d[k].view(np.int16) if d[k].dtype == np.uint16 else d[k]).cuda()
+           for k in keys}
+    base_d = torch.from_numpy(base.view(np.int16)).cuda()
+    wt_d = torch.from_numpy(wt.view(np.int16)).cuda()
+    lat = torch.empty((N, B - 1, R), dtype=torch.int16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(k, st=stream):
+        native.xpress_latent_pass(*(dev[x] for x in keys), lat, N, B, R, H, V, stream=st)
+        native.xpress_readout_gemm_argmax_to_blk(base_d, lat, wt_d, dev["blk"], N, B, V, R, V,
+                                                 stream=st)
+
+    def reserve(st):
+        # both entry points share the stream's workspace: size it outside
+        # capture with one eager pass on that stream
+        native.xpress_latent_reserve(N, B, R, H, stream=st)
+        step(0, st)
+        torch.cuda.synchronize()
+
+    reserve(stream)
+    if args.graph:
+        wall, region_gpu, n = time_graph(step, args.steps, args.warmup, args.graph, reserve)
+        args.steps = n
+        durs = [region_gpu / n]
+    else:
+        wall, region_gpu, durs = time_steps(step, args.steps, args.warmup, stream)
+    per_pass = region_gpu / args.steps
+    nbytes = lw.bytes_moved + gw.bytes_read
+    flops = lw.flops + gw.flops
+    achieved = nbytes / per_pass / 1e9
+    blk = dev["blk"].cpu().numpy()
+    return {
+        "metric": "one pass (latent stage + readout with in-place bias): passes/s and us per "
+                  "pass, N=%d B=%d R=%d H=%d V=%d" % (N, B, R, H, V),
+        "value": round(args.steps / wall, 1),
+        "unit": "passes/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "op": "pass", "latent": lname, "readout": gname,
+                   "N": N, "B": B, "R": R, "H": H, "V": V, "bytes_per_step": nbytes,
+                   "flops_per_step": flops, "launches_per_step": 5,
+                   "launch": ("hip graph of %d steps" % args.graph) if args.graph else "stream"},
+        "us_per_pass": round(per_pass * 1e6, 3),
+        "tflops": round(flops / per_pass / 1e12, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "note": "five kernels per pass; achieved over the pass's GPU time"},
+        "cpu_baseline": None,
+        "blk_in_range": bool(((blk[:, 1:] >= 0) & (blk[:, 1:] < V)).all()),
+        "anchor_kept": bool(np.array_equal(blk[:, 0], d["blk"][:, 0])),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--op", choices=["readout", "topc", "gemm", "latent"], default="readout")
+    ap.add_argument("--op", choices=["readout", "topc", "gemm", "latent", "pass"],
+                    default="readout")
     ap.add_argument("--graph", type=int, default=0,
                     help="capture this many steps per HIP graph and time graph replays")
     ap.add_argument("--topc-c", type=int, default=1024, choices=[64, 256, 1024, 4096])
@@ -535,6 +604,8 @@ def main():
         out = bench_gemm(args, np, torch, native, workloads)
     elif args.op == "latent":
         out = bench_latent(args, np, torch, native, workloads)
+    elif args.op == "pass":
+        out = bench_pass(args, np, torch, native, workloads)
     else:
         out = bench_readout(args, np, torch, native, workloads)
     print(json.dumps(out))

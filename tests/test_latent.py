@@ -83,7 +83,9 @@ class Tiles:
 
 
 SHAPES = [(1, 2, 64, 64), (3, 3, 64, 192), (7, 5, 128, 64), (33, 16, 192, 128),
-          (2, 31, 64, 64), (1, 32, 64, 64), (21, 7, 320, 576), (40, 16, 256, 512)]
+          (2, 31, 64, 64), (1, 32, 64, 64), (21, 7, 320, 576), (40, 16, 256, 512),
+          # 9 row tiles of 128 and of 8 blocks: XCD-grouped placement, padded to 16
+          (70, 16, 128, 256)]
 
 
 @pytest.mark.parametrize("tiles", [(1, 1, 1), (2, 2, 2), (4, 4, 4), (8, 8, 8)])

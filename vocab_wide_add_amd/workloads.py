@@ -387,6 +387,7 @@ LATENT_WORKLOADS = {
         LatentWorkload("latent_b32_n3_r128_h256_v1000", 3, 32, 128, 256, 1000, 33),
         LatentWorkload("latent_n1_b16_r256_h512_v152064", 1, 16, 256, 512, 152064, 34),
         LatentWorkload("latent_n64_b16_r256_h512_v152064", 64, 16, 256, 512, 152064, 35),
+        LatentWorkload("latent_n32_b16_r256_h512_v152064", 32, 16, 256, 512, 152064, 39),
         LatentWorkload("latent_n256_b16_r256_h512_v152064", 256, 16, 256, 512, 152064, 36),
         LatentWorkload("latent_exact_n64_b16_r256_h512_v152064", 64, 16, 256, 512, 152064,
                        37, "exact"),
@@ -396,6 +397,17 @@ LATENT_WORKLOADS = {
 }
 
 LATENT_BENCH_WORKLOAD = "latent_n256_b16_r256_h512_v152064"
+
+# One whole pass: the latent stage feeding the readout with in-place bias
+# (the latent rows are the readout matmul's x; blk is read and written in
+# place), as (latent workload, readout workload) of the same N, B, R and V.
+PASS_WORKLOADS = {
+    "pass_n32_b16_r256_h512_v152064": ("latent_n32_b16_r256_h512_v152064",
+                                       "gemm_normal_n32_b16_v152064_r256"),
+    "pass_n1_b16_r256_h512_v152064": ("latent_n1_b16_r256_h512_v152064",
+                                      "gemm_normal_n1_b16_v152064_r256"),
+}
+PASS_BENCH_WORKLOAD = "pass_n32_b16_r256_h512_v152064"
 
 
 def generate_latent(w: LatentWorkload):
