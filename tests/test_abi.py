@@ -275,3 +275,29 @@ def test_latent_no_blocks_is_ok_without_pointers():
     lib = native.load()
     args = _latent_args(N=0)
     assert lib.xpress_latent_pass(*([0] * 10 + args[10:]), None) == 0
+
+
+def test_binding_refuses_tensors_shorter_than_the_call():
+    """A tensor whose storage ends before the bytes a call touches is refused
+    before the library is called (a kernel would read past it)."""
+    import torch
+    t = torch.zeros(10, dtype=torch.int16)
+    native._span(t, 20, "t")
+    with pytest.raises(ValueError, match="storage holds 20"):
+        native._span(t, 22, "t")
+    v = t[4:]                      # 12 bytes from its first element
+    native._span(v, 12, "v")
+    with pytest.raises(ValueError, match="storage holds 12"):
+        native._span(v, 14, "v")
+    base = torch.zeros(2 * 100, dtype=torch.int16)
+    blk = torch.zeros(2 * 3, dtype=torch.int64)
+    with pytest.raises(ValueError, match="base"):
+        # 4 rows of 100 need 800 bytes, base holds 400
+        native.xpress_add_argmax_to_blk(base, base, blk, 2, 3, 100, 100, 100)
+    with pytest.raises(ValueError, match="lat_out"):
+        small = torch.zeros(8, dtype=torch.int16)
+        big = torch.zeros(1 << 20, dtype=torch.int16)
+        ids = torch.zeros(64, dtype=torch.int64)
+        native.xpress_latent_pass(ids, ids, big, big, big, big, big, big, big, small,
+                                  2, 4, 64, 64, 10)
+

@@ -128,11 +128,18 @@ def test_latent_no_blocks_and_errors():
     assert (out == 7).all()
     # misaligned weight, bad sizes, output overlapping an input: rejected
     bad = dict(dd)
-    bad["wg"] = dd["wg"].view(-1)[1:]
+    wg_pad = torch.zeros(dd["wg"].numel() + 8, dtype=torch.int16, device="cuda")
+    bad["wg"] = wg_pad[1:]      # long enough, but 2 bytes past a 16-byte boundary
     with pytest.raises(native.XpressError):
         native.xpress_latent_pass(*(bad[k] for k in KEYS), out, w.N, w.B, w.R, w.H, w.V)
+    # sizes the library rejects (R not a multiple of 64), passed as bare
+    # addresses so that the binding's own span check does not catch it first
     with pytest.raises(native.XpressError):
-        native.xpress_latent_pass(*(dd[k] for k in KEYS), out, w.N, w.B, 96, w.H, w.V)
+        native.xpress_latent_pass(*(dd[k].data_ptr() for k in KEYS), out.data_ptr(), w.N, w.B,
+                                  96, w.H, w.V)
+    # a tensor too short for the sizes is refused by the binding
+    with pytest.raises(ValueError):
+        native.xpress_latent_pass(*(dd[k] for k in KEYS), out, w.N, w.B, 2 * w.R, w.H, w.V)
     with pytest.raises(native.XpressError):
         native.xpress_latent_pass(*(dd[k] for k in KEYS), dd["xh"], w.N, w.B, w.R, w.H, w.V)
     torch.cuda.synchronize()

@@ -3,8 +3,10 @@
 Argument marshalling only: every step of the readout runs in the library's
 HIP kernels.  Entry points keep the C names.  Tensor arguments may be torch
 tensors on a GPU (their ``data_ptr()`` is passed) or plain integer device
-addresses.  A nonzero status raises :class:`XpressError`.  If the library has
-not been built, the first call raises -- there is no fallback path.
+addresses; for a tensor the binding also checks that its storage covers the
+bytes the call will touch, which a bare pointer cannot tell the library.  A
+nonzero status raises :class:`XpressError`.  If the library has not been
+built, the first call raises -- there is no fallback path.
 """
 from __future__ import annotations
 
@@ -102,6 +104,18 @@ def _ptr(x):
     raise TypeError("expected a GPU tensor or an integer address, got %r" % type(x))
 
 
+def _span(t, nbytes: int, what: str):
+    """Refuse a tensor whose storage ends before the ``nbytes`` the call
+    will touch from its first element (integer addresses are the caller's
+    responsibility, as in the C ABI)."""
+    if nbytes <= 0 or t is None or isinstance(t, int) or not hasattr(t, "untyped_storage"):
+        return
+    avail = t.untyped_storage().nbytes() - t.storage_offset() * t.element_size()
+    if nbytes > avail:
+        raise ValueError("%s: the call reads or writes %d bytes from the tensor's first "
+                         "element, its storage holds %d" % (what, nbytes, avail))
+
+
 def _stream(stream):
     """HIP stream handle: None means torch's current stream on the current device."""
     if stream is None:
@@ -124,6 +138,11 @@ def xpress_add_argmax_to_blk(base, bias, blk, N: int, B: int, V: int,
     Queued on ``stream`` (default: torch's current stream).  See the header
     for the layout rules and error behaviour.
     """
+    rows = int(N) * (int(B) - 1)
+    if rows > 0:
+        _span(base, ((rows - 1) * int(stride_base_r) + int(V)) * 2, "base")
+        _span(bias, ((rows - 1) * int(stride_bias_r) + int(V)) * 2, "bias")
+        _span(blk, int(N) * int(B) * 8, "blk")
     lib = load()
     _check(lib.xpress_add_argmax_to_blk(_ptr(base), _ptr(bias), _ptr(blk), int(N), int(B),
                                         int(V), int(stride_base_r), int(stride_bias_r),
@@ -135,6 +154,12 @@ def xpress_topc_argmax_to_blk(base_c, bias_c, cand, blk, N: int, B: int, C: int,
                               stream=None) -> None:
     """blk[n, 1+j] = cand[r, argmax_c bf16(base_c[r, c] + bias_c[r, c])],
     r = n*(B-1) + j; base_c, bias_c, cand are [N, B-1, C] contiguous."""
+    rows = int(N) * (int(B) - 1)
+    if rows > 0:
+        _span(base_c, rows * int(C) * 2, "base_c")
+        _span(bias_c, rows * int(C) * 2, "bias_c")
+        _span(cand, rows * int(C) * 8, "cand")
+        _span(blk, int(N) * int(B) * 8, "blk")
     lib = load()
     _check(lib.xpress_topc_argmax_to_blk(_ptr(base_c), _ptr(bias_c), _ptr(cand), _ptr(blk),
                                          int(N), int(B), int(C), _stream(stream)),
@@ -145,6 +170,12 @@ def xpress_readout_gemm_argmax_to_blk(base, x, w, blk, N: int, B: int, V: int, R
                                       stride_base_r: int, stream=None) -> None:
     """blk[n, 1+b] = argmax_v bf16(base[r, v] + bf16(x[r] . w[v])), r = n*(B-1) + b;
     x is [rows, R], w is [V, R], all bf16 on the GPU."""
+    rows = int(N) * (int(B) - 1)
+    if rows > 0:
+        _span(base, ((rows - 1) * int(stride_base_r) + int(V)) * 2, "base")
+        _span(x, rows * int(R) * 2, "x")
+        _span(w, int(V) * int(R) * 2, "w")
+        _span(blk, int(N) * int(B) * 8, "blk")
     lib = load()
     _check(lib.xpress_readout_gemm_argmax_to_blk(_ptr(base), _ptr(x), _ptr(w), _ptr(blk),
                                                  int(N), int(B), int(V), int(R),
@@ -158,6 +189,14 @@ def xpress_latent_pass(blk, am1, xh, w1, wlat, mixl, wg, wu, wd, lat_out, N: int
     blk [N, B], am1 [N] (int64), the hidden cache xh [N, B, R], the embedding
     w1 [V, R] and the out-major weights wlat [R, R], mixl [B, B, R],
     wg / wu [H, R], wd [R, H] (all bf16 on the GPU)."""
+    n, b, r, h, v = int(N), int(B), int(R), int(H), int(V)
+    if n > 0:
+        for t, nb, what in ((blk, n * b * 8, "blk"), (am1, n * 8, "am1"),
+                            (xh, n * b * r * 2, "xh"), (w1, v * r * 2, "w1"),
+                            (wlat, r * r * 2, "wlat"), (mixl, b * b * r * 2, "mixl"),
+                            (wg, h * r * 2, "wg"), (wu, h * r * 2, "wu"), (wd, r * h * 2, "wd"),
+                            (lat_out, n * (b - 1) * r * 2, "lat_out")):
+            _span(t, nb, what)
     lib = load()
     _check(lib.xpress_latent_pass(_ptr(blk), _ptr(am1), _ptr(xh), _ptr(w1), _ptr(wlat),
                                   _ptr(mixl), _ptr(wg), _ptr(wu), _ptr(wd), _ptr(lat_out),
@@ -171,7 +210,8 @@ def xpress_latent_reserve(N: int, B: int, R: int, H: int, stream=None) -> None:
 
 
 def xpress_latent_set_tiles(mix: int = 0, gate: int = 0, down: int = 0) -> None:
-    """Row-slab counts (1, 2, 4; 0 = automatic) of the three latent kernels."""
+    """Row-slab counts of the three latent kernels: 1, 2 or 4 (direct kernels),
+    8 (LDS-staged kernels), 0 = automatic."""
     _check(load().xpress_latent_set_tiles(int(mix), int(gate), int(down)),
            "xpress_latent_set_tiles")
 
@@ -204,6 +244,8 @@ def xpress_describe_plan(base, bias, N: int, B: int, V: int, stride_base_r: int,
 
 def xpress_bf16_add_round_table(a_vals, n_a: int, out, stream=None) -> None:
     """out[i*65536 + b] = bf16(a_vals[i] + b) on the GPU, for every pattern b."""
+    _span(a_vals, int(n_a) * 2, "a_vals")
+    _span(out, int(n_a) * 65536 * 2, "out")
     _check(load().xpress_bf16_add_round_table(_ptr(a_vals), int(n_a), _ptr(out),
                                               _stream(stream)),
            "xpress_bf16_add_round_table")
