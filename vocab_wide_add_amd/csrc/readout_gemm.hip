@@ -182,10 +182,13 @@ __global__ __launch_bounds__(KW * 64) void gemm_readout_kernel(GemmArgs a)
     // copy) rather than kept in registers, which the x operands fill.
     // base: each wave copies its own rows (instruction j: rows 16j .. 16j+15
     // of the wave's, lane l row 16j + l/4, logical 16-byte column
-    // (l % 4) ^ (row % 4)); only that wave reads them back.  Rows past the
-    // last read the last row and are never used.
+    // (l % 4) ^ ((row / 4) % 4)); only that wave reads them back.  A row is
+    // 64 bytes, so rows 4 apart share LDS banks: keying the swizzle on
+    // row / 4 spreads the 32 rows of one epilogue read over all 16 bank
+    // groups (two rows each) where row % 4 left 8 rows on each of 4.  Rows
+    // past the last read the last row and are never used.
     const uint32_t b_lrow = lane >> 2;
-    const uint32_t b_col = 8u * ((lane & 3u) ^ (b_lrow & 3u));
+    const uint32_t b_col = 8u * ((lane & 3u) ^ ((b_lrow >> 2) & 3u));
     auto dma_base = [&](uint32_t t, int buf) {
 #pragma unroll
         for (int j = 0; j < BLOADS; ++j) {
@@ -316,7 +319,7 @@ __global__ __launch_bounds__(KW * 64) void gemm_readout_kernel(GemmArgs a)
             const uint32_t lrow = wave * WROWS + 32u * g + (lane & 31u);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const uint32_t pc = (uint32_t)q ^ (lrow & 3u);
+                const uint32_t pc = (uint32_t)q ^ ((lrow >> 2) & 3u);
                 bv[q] = *reinterpret_cast<const u32x2*>(
                     base_buf(i % kRing) + lrow * kTileV + pc * 8u + 4u * khalf);
             }
