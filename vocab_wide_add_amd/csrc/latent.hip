@@ -463,16 +463,19 @@ __global__ void __launch_bounds__(kThreads) latent_down_kernel(DownArgs a)
 // lanes per 128-byte row segment, so every load instruction reads eight whole
 // cache lines), four chunks in flight at once, and the matrix cores read
 // their operands back with 16-byte LDS loads.  Within an LDS row the 16-byte
-// columns are permuted by XOR with (row & 7) so that the 32 rows an operand
-// load touches spread over the LDS banks.
+// columns are permuted by XOR with ((row >> 1) & 7): a row is 128 bytes, so
+// rows two apart share banks, and keying on row >> 1 puts the 16 rows one
+// pass of an operand load touches on 16 different bank groups (row & 7 left
+// them two to a group).
 // ---------------------------------------------------------------------------
 constexpr int kKC = 64;           // contraction elements per chunk
 constexpr int kRing = 4;          // chunks in flight
 constexpr int kSlabRows = 128;    // A rows of a staged workgroup
 
 // Rows [32 j + 8 w, +8) of a chunk are loaded by wave w's j-th instruction;
-// lane l reads row 32 j + 8 w + l / 8, logical 16-byte column (l % 8) ^ (l / 8),
-// and lands in LDS at row-major position (row, l % 8).
+// lane l reads row 32 j + 8 w + l / 8, logical 16-byte column
+// (l % 8) ^ ((row >> 1) & 7), and lands in LDS at row-major position
+// (row, l % 8).
 template <int ROWS>
 struct DmaRows {
     static constexpr int kN = ROWS / 32;  // load instructions per wave per chunk
@@ -493,18 +496,20 @@ __device__ __forceinline__ void dma_chunk(const DmaRows<ROWS>& d, uint16_t* lds_
 __device__ __forceinline__ bf16x8 lds_operand(const uint16_t* lds_slot, int r0, int s, int lane)
 {
     const int r = r0 + (lane & 31);
-    const int q = (2 * s + (lane >> 5)) ^ (r & 7);
+    const int q = (2 * s + (lane >> 5)) ^ ((r >> 1) & 7);
     return __builtin_bit_cast(bf16x8,
                               *reinterpret_cast<const u32x4*>(lds_slot + r * kKC + 8 * q));
 }
 
 template <int ROWS>
 __device__ __forceinline__ void dma_setup(DmaRows<ROWS>& d, const uint16_t* const* row_base,
-                                          int lane)
+                                          int lane, int wave)
 {
+    // the row 32 j + 8 wave + lane / 8 has (row >> 1) & 7 = (4 wave + lane / 16) & 7
+    const int sw = (4 * wave + (lane >> 4)) & 7;
 #pragma unroll
     for (int j = 0; j < DmaRows<ROWS>::kN; ++j) {
-        d.src[j] = row_base[j] + 8 * ((lane & 7) ^ (lane >> 3));
+        d.src[j] = row_base[j] + 8 * ((lane & 7) ^ sw);
     }
 }
 
@@ -598,8 +603,8 @@ __global__ void __launch_bounds__(kThreads) latent_gate_staged(GateArgs a)
     }
     DmaRows<kSlabRows> da;
     DmaRows<kB> db;
-    dma_setup(da, abase, lane);
-    dma_setup(db, bbase, lane);
+    dma_setup(da, abase, lane, wave);
+    dma_setup(db, bbase, lane, wave);
     f32x16 acc[2 * NH] = {};
     staged_mma<kSlabRows, kB, 2 * NH>(acc, da, db, lds_a, lds_b, (int)(a.R / kKC), tid, 0u);
 #pragma unroll
@@ -642,8 +647,8 @@ __global__ void __launch_bounds__(kThreads) latent_down_staged(DownArgs a)
     const uint16_t* bbase[1] = {a.wd + (size_t)(c0 + 8 * wave + (lane >> 3)) * a.H};
     DmaRows<kSlabRows> da;
     DmaRows<kTile> db;
-    dma_setup(da, abase, lane);
-    dma_setup(db, bbase, lane);
+    dma_setup(da, abase, lane, wave);
+    dma_setup(db, bbase, lane, wave);
     f32x16 acc[1] = {};
     staged_mma<kSlabRows, kTile, 1>(acc, da, db, lds_a, lds_b, (int)(a.H / kKC), tid, 0u);
 #pragma unroll
@@ -724,8 +729,8 @@ __global__ void __launch_bounds__(kThreads) latent_mix_staged(MixArgs a)
     const uint16_t* bbase[1] = {a.wlat + (size_t)(c0 + 8 * wave + (lane >> 3)) * R};
     DmaRows<kSlabRows> da;
     DmaRows<kTile> db;
-    dma_setup(da, abase, lane);
-    dma_setup(db, bbase, lane);
+    dma_setup(da, abase, lane, wave);
+    dma_setup(db, bbase, lane, wave);
     f32x16 acc[1] = {};
     staged_mma<kSlabRows, kTile, 1>(acc, da, db, lds_a, lds_b, (int)(R / kKC), tid, zero_row);
     // x = cache + projection, into LDS over the A staging area (free after
