@@ -1,0 +1,91 @@
+"""The benchmark's host-side contract, on the CPU: one GPU only, a JSON line
+with the fields the roofline and traffic reports need, and traffic figures
+reported only while the kernel code they were counted on is unchanged."""
+import importlib.util
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+from conftest import gpu_available
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _run(args, env_extra=None):
+    env = dict(os.environ)
+    env.update(env_extra or {})
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")] + args, cwd=ROOT,
+                          env=env, capture_output=True, text=True, timeout=300)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = _run(["--gpus", "2"])
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    r = _run([], {"WORLD_SIZE": "4"})
+    assert r.returncode == 2
+
+
+@pytest.mark.skipif(gpu_available(), reason="checks the no-GPU exit")
+def test_no_gpu_exits_with_a_message():
+    r = _run(["--steps", "1", "--warmup", "0"])
+    assert r.returncode == 1
+    assert "needs a GPU" in r.stderr
+
+
+def test_code_digest_ignores_comments_only(tmp_path):
+    b = _bench()
+    a = tmp_path / "a.hip"
+    a.write_text("int f(int x) { return x + 1; }  // one\n/* block */\n")
+    c = tmp_path / "c.hip"
+    c.write_text("// another comment\nint f(int x)\n{\n    return x + 1;\n}\n")
+    d = tmp_path / "d.hip"
+    d.write_text("int f(int x) { return x + 2; }\n")
+    assert b.source_digest(str(a)) == b.source_digest(str(c))
+    assert b.source_digest(str(a)) != b.source_digest(str(d))
+
+
+def test_traffic_records_are_reported_only_for_their_code():
+    """A committed counter record is reported while the kernel code it was
+    counted on is unchanged, and not otherwise; its figures add up."""
+    b = _bench()
+    assert b.traffic_for("no_such_workload") is None
+    for name, src in (("spike_n32_b16_v152064", b.SRC),
+                      ("gemm_normal_n32_b16_v152064_r256", b.GEMM_SRC)):
+        with open(os.path.join(ROOT, "profiles", "traffic_%s.json" % name)) as f:
+            t = json.load(f)
+        fresh = t["kernel_source_sha256"] == b.source_digest(src)
+        assert b.traffic_for(name, src) == (t["hbm_bytes_per_launch"] if fresh else None)
+        assert t["hbm_bytes_per_launch"] == t["hbm_fetch_bytes_per_launch"] + \
+            t["hbm_write_bytes_per_launch"]
+        ratio = t["hbm_bytes_per_launch"] / t["algorithmic_bytes_per_launch"]
+        assert abs(ratio - t["traffic_over_algorithmic"]) < 1e-3
+
+
+def test_result_line_fields():
+    b = _bench()
+    out = b.result_line("m", "w", {"workload": "w"}, bytes_per_call=4_000_000, rows=10,
+                        steps=100, warmup=5, wall=1e-3, region_gpu=0.9e-3,
+                        durs=[9e-6] * 100, launches=1, traffic=None)
+    for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+              "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+              "roofline", "cpu_baseline"):
+        assert k in out, k
+    r = out["roofline"]
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
+    # 4 MB per launch over 9 us per launch of GPU time
+    assert abs(r["achieved"] - 4_000_000 / 9e-6 / 1e9) < 1.0
+    assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
+    # whole-job rate over the wall clock: 100 steps of 4 MB in 1 ms
+    assert abs(out["value"] - 400.0) < 1e-6
+    assert out["n_gpus"] == 1 and out["steps"] == 100
