@@ -145,6 +145,46 @@ def test_gemm_several_workgroups_per_range(N, B, V, R):
     assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("R", [64, 256])
+def test_gemm_special_values(R):
+    """Special base values against the oracle (dyadic x and w, so the bias is
+    exact): all -inf rows (id 0 wins), all +inf rows and +inf ties (the
+    lowest id), -0 next to +0 sums, subnormal sums, the largest finite bf16
+    next to a positive bias (overflow to +inf), winners in the ragged last
+    tile, and zero x rows (bias exactly +0)."""
+    N, B, V = 4, 9, 1000               # 32 rows, a ragged last tile
+    rows = N * (B - 1)
+    g = np.random.Generator(np.random.PCG64(4040 + R))
+    base = workloads.f32_to_bf16_bits((g.integers(-8, 9, size=(rows, V)) / 4.0).astype(np.float32))
+    x = workloads.f32_to_bf16_bits((g.integers(-8, 9, size=(rows, R)) / 8.0).astype(np.float32))
+    wt = workloads.f32_to_bf16_bits((g.integers(-8, 9, size=(V, R)) / 8.0).astype(np.float32))
+    NEG_INF, POS_INF, NEG_ZERO, MAX_FIN = 0xFF80, 0x7F80, 0x8000, 0x7F7F
+    base[0, :] = NEG_INF                          # all -inf
+    base[1, :] = POS_INF                          # all +inf
+    base[2, [500, 700]] = POS_INF                 # +inf tie
+    x[3, :] = 0                                   # bias +0 everywhere
+    base[3, :] = NEG_ZERO                         # -0 + +0 = +0 everywhere: id 0
+    x[4, :] = 0
+    base[4, :] = 0xBF80                           # -1.0 ...
+    base[4, 999] = 0x0001                         # ... a subnormal at the last id
+    base[4, 998] = 0x8001
+    base[5, [10, 20]] = MAX_FIN                   # overflow with a positive bias
+    base[6, 992:] = POS_INF                       # only the ragged tile holds +inf
+    base[7, :] = NEG_INF
+    base[7, 31] = 0                               # one finite value at a tile edge
+    blk0 = np.full((N, B), -1, dtype=np.int64)
+    blk0[:, 0] = 5
+    want = blk0.copy()
+    want[:, 1:] = oracle.gemm_argmax_rows(base, x, wt, range(rows), V, R, V,
+                                          threads=ORACLE_THREADS).reshape(N, B - 1)
+    w1 = want[:, 1:].reshape(-1)
+    assert w1[0] == 0 and w1[1] == 0 and w1[2] == 500 and w1[3] == 0 and w1[4] == 999
+    assert w1[6] == 992 and w1[7] == 31
+    say("gemm special values R=%d" % R)
+    got = gpu_gemm(to_dev(base), to_dev(x), to_dev(wt), blk0, N, B, V, R, V)
+    assert np.array_equal(got, want)
+
+
 def test_gemm_repeated_calls_and_guard_cells():
     import torch
     N, B, V, R = 4, 16, 20000, 128
