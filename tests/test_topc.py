@@ -150,3 +150,40 @@ def test_topc_default_plan_ragged_and_unaligned(C, offset):
                                      dc.data_ptr() + 8 * offset, blk_d, N, B, C)
     torch.cuda.synchronize()
     assert np.array_equal(blk_d.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("C", [64, 256, 1024])    # one wave per row up to 256, else streaming
+def test_topc_special_values(C):
+    """Special values against the oracle on both top-C paths: all -inf rows
+    (position 0's id wins), +inf ties (the lowest position), -0 before +0,
+    subnormal sums, overflow to +inf, and a winner at the last position;
+    candidate ids are large and distinct so that a position slip shows."""
+    N, B = 3, 9
+    rows = N * (B - 1)
+    g = np.random.Generator(np.random.PCG64(5050 + C))
+    base_c = workloads.f32_to_bf16_bits((g.integers(-8, 9, size=(rows, C)) / 4.0).astype(np.float32))
+    bias_c = workloads.f32_to_bf16_bits((g.integers(-4, 5, size=(rows, C)) / 8.0).astype(np.float32))
+    cand = (g.permutation(rows * C).astype(np.int64).reshape(rows, C) + (1 << 33))
+    NEG_INF, POS_INF, NEG_ZERO, MAX_FIN = 0xFF80, 0x7F80, 0x8000, 0x7F7F
+    base_c[0, :] = NEG_INF
+    bias_c[0, :] = 0
+    base_c[1, [C // 3, C - 1]] = POS_INF
+    base_c[2, :] = NEG_ZERO
+    bias_c[2, :] = NEG_ZERO                       # every sum is -0: position 0 wins
+    base_c[3, :] = NEG_ZERO
+    bias_c[3, :] = 0
+    bias_c[3, C // 2] = NEG_ZERO                  # -0 + -0 = -0 ties +0: position 0
+    base_c[4, :] = 0xBF80
+    bias_c[4, :] = 0
+    base_c[4, C - 1] = 0x0001                     # a subnormal at the last position
+    base_c[5, [1, C - 2]] = MAX_FIN
+    bias_c[5, [1, C - 2]] = MAX_FIN               # both overflow to +inf: position 1
+    blk0 = np.full((N, B), -1, dtype=np.int64)
+    blk0[:, 0] = 77
+    want = oracle_topc(base_c, bias_c, cand, blk0, N, B, C)
+    w1 = want[:, 1:].reshape(-1)
+    assert w1[0] == cand[0, 0] and w1[1] == cand[1, C // 3] and w1[2] == cand[2, 0]
+    assert w1[3] == cand[3, 0] and w1[4] == cand[4, C - 1] and w1[5] == cand[5, 1]
+    say("topc special values C=%d" % C)
+    got = gpu_topc(to_dev(base_c), to_dev(bias_c), to_dev(cand), blk0, N, B, C)
+    assert np.array_equal(got, want)
