@@ -258,3 +258,28 @@ def test_gemm_graph_replay_matches_eager(N, B, V, R):
         want[:, 1:] = oracle.gemm_argmax_rows(base, x, wt, range(rows), V, R, V,
                                               threads=ORACLE_THREADS).reshape(N, B - 1)
         assert np.array_equal(got, want), rep
+
+
+def test_gemm_two_streams_at_once():
+    """Calls on two streams at once each use their own (device, stream) key
+    table: both results must match the oracle."""
+    import torch
+    cases = []
+    for k, (N, B, V, R) in enumerate([(6, 16, 4000, 128), (9, 16, 3000, 128)]):
+        rows = N * (B - 1)
+        base, x, wt = _dyadic(rows, V, R, seed=900 + k)
+        blk0 = np.full((N, B), -1, dtype=np.int64)
+        blk0[:, 0] = k
+        want = blk0.copy()
+        want[:, 1:] = oracle.gemm_argmax_rows(base, x, wt, range(rows), V, R, V,
+                                              threads=ORACLE_THREADS).reshape(N, B - 1)
+        cases.append((N, B, V, R, to_dev(base), to_dev(x), to_dev(wt), to_dev(blk0), want))
+    s = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    say("gemm two streams")
+    for _ in range(5):
+        for (N, B, V, R, bd, xd, wd, blk, _), st in zip(cases, s):
+            native.xpress_readout_gemm_argmax_to_blk(bd, xd, wd, blk, N, B, V, R, V, stream=st)
+    torch.cuda.synchronize()
+    for (N, B, V, R, bd, xd, wd, blk, want) in cases:
+        assert np.array_equal(blk.cpu().numpy(), want)
