@@ -360,6 +360,9 @@ def bench_gemm(args, np, torch, native, workloads):
                       w.rows, args.steps, args.warmup, wall, region_gpu, durs, 2,
                       traffic_for(name, GEMM_SRC))
     out["tflops"] = round(w.flops * args.steps / wall / 1e12, 2)
+    out["roofline"]["note"] = ("two launches per pass (the fused kernel and the key "
+                               "reduction); achieved is over the pass's GPU time, and "
+                               "kernel_us_region_avg is that time over both launches")
 
     # context: the unfused path -- a library matmul writing the bf16 bias,
     # then this library's readout over base and that bias
