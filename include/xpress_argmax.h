@@ -79,6 +79,10 @@ extern "C" {
  * call, so repeated calls and graph replays need no clearing.  Calls queued
  * on different streams use different workspaces and may run concurrently.
  * The caller keeps every buffer alive until the queued work has finished.
+ * Host threads: the library's own tables are locked, but a call holds its
+ * stream's workspace from lookup to launch, so calls that queue on one
+ * stream come from one host thread at a time, and xpress_release runs while
+ * no other call of the library is in progress on any thread.
  */
 int xpress_add_argmax_to_blk(const uint16_t* base, const uint16_t* bias,
                              int64_t* blk, int64_t N, int64_t B, int64_t V,
@@ -242,7 +246,9 @@ int xpress_latent_set_tiles(int mix, int gate, int down);
 /*
  * xpress_release -- free every workspace the library holds on the current
  * device (after synchronising that device).  Optional; for tests and for
- * callers that want the memory back.
+ * callers that want the memory back.  No other call of the library may be in
+ * progress meanwhile, and graphs captured before hold freed workspace and
+ * must not be replayed; the next call allocates afresh.
  */
 int xpress_release(void);
 
