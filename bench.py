@@ -121,7 +121,7 @@ def copy_probe(nbytes: int, reps: int):
 def time_graph(step, steps: int, warmup: int, per_graph: int, reserve):
     """Capture ``per_graph`` steps into one HIP graph and time ``steps``
     steps as graph replays (region 1: wall clock and one HIP event pair
-    around the replays).  Returns (wall seconds, GPU seconds, None)."""
+    around the replays).  Returns (wall seconds, GPU seconds, steps replayed)."""
     import torch
     cap = torch.cuda.Stream()
     reserve(cap)
@@ -218,6 +218,7 @@ def result_line(metric, name, config, bytes_per_call, rows, steps, warmup, wall,
         "region_gpu_us_per_step": round(region_gpu / steps * 1e6, 3),
         "kernel_us_region_avg": round(kernel_avg * 1e6, 3),
         "kernel_us_event_pairs": {"avg": round(kavg * 1e6, 3), "min": round(durs[0] * 1e6, 3),
+                                  "p10": round(durs[int(len(durs) * 0.1)] * 1e6, 3),
                                   "p50": round(durs[len(durs) // 2] * 1e6, 3),
                                   "p90": round(durs[int(len(durs) * 0.9)] * 1e6, 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -448,7 +449,9 @@ def bench_latent(args, np, torch, native, workloads):
         "us_per_pass": round(per_pass * 1e6, 3),
         "pass_us_event_pairs": {"avg": round(sum(durs) / len(durs) * 1e6, 3),
                                 "min": round(durs[0] * 1e6, 3),
-                                "p50": round(durs[len(durs) // 2] * 1e6, 3)},
+                                "p10": round(durs[int(len(durs) * 0.1)] * 1e6, 3),
+                                "p50": round(durs[len(durs) // 2] * 1e6, 3),
+                                "p90": round(durs[int(len(durs) * 0.9)] * 1e6, 3)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 5), "traffic": None,

@@ -89,3 +89,5 @@ def test_result_line_fields():
     # whole-job rate over the wall clock: 100 steps of 4 MB in 1 ms
     assert abs(out["value"] - 400.0) < 1e-6
     assert out["n_gpus"] == 1 and out["steps"] == 100
+    k = out["kernel_us_event_pairs"]
+    assert k["min"] <= k["p10"] <= k["p50"] <= k["p90"]
