@@ -185,6 +185,55 @@ def test_gemm_special_values(R):
     assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("N,B,R", [(3, 8, 256),     # 21 rows: one wave per workgroup
+                                   (10, 10, 64),    # 90 rows: two waves
+                                   (20, 16, 256),   # 300 rows: eight waves
+                                   (20, 16, 128)])
+def test_gemm_non_positive_maxima(N, B, R):
+    """Rows whose maximum is not positive, beside rows whose maximum is, in
+    every launch shape: all-negative rows full of ties, rows whose maximum
+    is +0 reached from -0 and +0 base values, -inf rows, and rows negative
+    over the first part of the vocabulary only (so that some vocabulary
+    ranges of a row have a positive maximum and others not).  Dyadic inputs,
+    so the bias is exact and the oracle's result is the only correct one."""
+    V = 3000                                   # a ragged last tile
+    rows = N * (B - 1)
+    base, x, wt = _dyadic(rows, V, R, seed=7000 + rows + R)
+    g = np.random.Generator(np.random.PCG64(7100 + rows + R))
+    NEG_INF, NEG_ZERO = 0xFF80, 0x8000
+    kinds = []
+    for r in range(rows):
+        k = r % 5
+        kinds.append(k)
+        if k == 1:       # all negative, many ties at the top value
+            x[r, :] = 0
+            base[r, :] = workloads.f32_to_bf16_bits(
+                (-g.integers(1, 5, size=V) / 4.0).astype(np.float32))
+        elif k == 2:     # maximum +0, from -0 and +0 base values
+            x[r, :] = 0
+            base[r, :] = workloads.f32_to_bf16_bits(np.full(V, -0.5, np.float32))
+            zpos = g.choice(V, size=6, replace=False)
+            base[r, zpos[:3]] = NEG_ZERO
+            base[r, zpos[3:]] = 0
+        elif k == 3:     # -inf everywhere but one negative value
+            base[r, :] = NEG_INF
+            base[r, g.integers(0, V)] = workloads.f32_to_bf16_bits(np.float32(-3.0))
+        elif k == 4:     # negative over the first part, positive after
+            cut = int(g.integers(V // 4, 3 * V // 4))
+            x[r, :] = 0
+            base[r, :cut] = workloads.f32_to_bf16_bits(np.full(cut, -1.0, np.float32))
+    blk0 = np.full((N, B), -1, dtype=np.int64)
+    blk0[:, 0] = 3
+    want = blk0.copy()
+    want[:, 1:] = oracle.gemm_argmax_rows(base, x, wt, range(rows), V, R, V,
+                                          threads=ORACLE_THREADS).reshape(N, B - 1)
+    say("gemm non-positive maxima N=%d B=%d R=%d" % (N, B, R))
+    got = gpu_gemm(to_dev(base), to_dev(x), to_dev(wt), blk0, N, B, V, R, V)
+    assert np.array_equal(got, want), [
+        (r, kinds[r], got[:, 1:].reshape(-1)[r], want[:, 1:].reshape(-1)[r])
+        for r in range(rows) if got[:, 1:].reshape(-1)[r] != want[:, 1:].reshape(-1)[r]][:8]
+
+
 def test_gemm_repeated_calls_and_guard_cells():
     import torch
     N, B, V, R = 4, 16, 20000, 128

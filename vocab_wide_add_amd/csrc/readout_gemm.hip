@@ -35,6 +35,15 @@
 //   * the workgroups that cover the row groups of one vocabulary range are
 //     placed on one XCD (workgroup b runs on XCD b mod 8), so each w tile is
 //     fetched from HBM once and served from that XCD's L2 afterwards;
+//   * in the 8-wave shape the epilogue keeps a tile's first maximum in one
+//     integer max per logit: a widened bf16 sum has 16 zero low bits, which
+//     take a tag that falls with the id's position in the tile, so among
+//     equal values the earlier id has the larger bit pattern; the running
+//     (value, id) is updated once per tile.  For positive values the bit patterns order as
+//     the values do (+inf included), so this is exact wherever a lane's
+//     maximum over its range is positive; a workgroup in which some lane's
+//     maximum is not (zero, negative, -inf) runs its range again with the
+//     per-logit compare-and-select epilogue, which is exact for every value;
 //   * per (row, range) the packed (value, ~id) key goes to a key table and the
 //     library's second pass reduces each row's keys into blk.
 // Numerics: the fp32 accumulation order of the MFMA is the hardware's; where
@@ -302,11 +311,14 @@ __global__ __launch_bounds__(KW * 64) void gemm_readout_kernel(GemmArgs a)
     const uint32_t first_id = t0 * kTileV + 4u * khalf;
     float best[kGroups];
     uint32_t bidx[kGroups];
+    auto reset_best = [&]() {
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g) {
-        best[g] = -__builtin_inff();
-        bidx[g] = (T > 0 && first_id < a.V) ? 0u : kNoIndex;
-    }
+        for (int g = 0; g < kGroups; ++g) {
+            best[g] = -__builtin_inff();
+            bidx[g] = (T > 0 && first_id < a.V) ? 0u : kNoIndex;
+        }
+    };
+    reset_best();
 
     f32x16 acc[kGroups];
     // Base of group g's rows in tile i, four consecutive ids per entry: from
@@ -349,12 +361,13 @@ __global__ __launch_bounds__(KW * 64) void gemm_readout_kernel(GemmArgs a)
     // from different waves slow each other down.  Full tiles run in the loop;
     // a ragged last tile runs after it, where x is no longer live, so its
     // clamped loads do not compete with x for registers.
-    auto step = [&](int i, auto full_tag, auto steady_tag, auto ng_tag) {
+    auto step = [&](int i, auto full_tag, auto steady_tag, auto ng_tag, auto exact_tag) {
         constexpr bool FULL = decltype(full_tag)::value;
         constexpr int NG = decltype(ng_tag)::value;  // row groups in use
         // steady: tile i + AHEAD exists and is full, so the copies and the
         // wait count are the fixed ones and the body has no branches
         constexpr bool STEADY = decltype(steady_tag)::value;
+        constexpr bool EXACT = decltype(exact_tag)::value;  // compare-and-select epilogue
         const uint32_t tv = (t0 + (uint32_t)i) * kTileV;
         // base copies now, w copies between the two groups' epilogues: each
         // wave's copies go to the address unit in two smaller bursts
@@ -409,33 +422,74 @@ __global__ __launch_bounds__(KW * 64) void gemm_readout_kernel(GemmArgs a)
             if (g >= NG) break;
             u32x2 bv[4];
             load_bv(g, i, tv, full_tag, bv);
-            // Within the tile a candidate's id is its position in the tile,
-            // an immediate operand of the select (a wave-uniform id would
-            // have to be copied into a vector register for every candidate:
-            // a select reads at most one scalar operand, and the condition
-            // is one); the running id is held relative to the tile meanwhile
-            // (wrapping arithmetic) and restored after the tile.
-            float tb = best[g];
-            uint32_t tp = bidx[g] - (uint32_t)(kTileV * i);
+            if constexpr (EXACT) {
+                // Within the tile a candidate's id is its position in the
+                // tile, an immediate operand of the select (a wave-uniform id
+                // would have to be copied into a vector register for every
+                // candidate: a select reads at most one scalar operand, and
+                // the condition is one); the running id is held relative to
+                // the tile meanwhile (wrapping arithmetic) and restored after
+                // the tile.
+                float tb = best[g];
+                uint32_t tp = bidx[g] - (uint32_t)(kTileV * i);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t s01 =
-                    add_round2(bv[q].x, round_pack2(acc[g][4 * q], acc[g][4 * q + 1]));
-                const uint32_t s23 =
-                    add_round2(bv[q].y, round_pack2(acc[g][4 * q + 2], acc[g][4 * q + 3]));
-                const float sv[4] = {bf16_lo(s01), bf16_hi(s01), bf16_lo(s23), bf16_hi(s23)};
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t s01 =
+                        add_round2(bv[q].x, round_pack2(acc[g][4 * q], acc[g][4 * q + 1]));
+                    const uint32_t s23 =
+                        add_round2(bv[q].y, round_pack2(acc[g][4 * q + 2], acc[g][4 * q + 3]));
+                    const float sv[4] = {bf16_lo(s01), bf16_hi(s01), bf16_lo(s23),
+                                         bf16_hi(s23)};
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    // ids past V exist only in a ragged last tile
-                    const bool take =
-                        FULL ? (sv[jj] > tb)
-                             : ((tv + 8u * q + 4u * khalf + jj < a.V) && (sv[jj] > tb));
-                    tb = take ? sv[jj] : tb;
-                    tp = take ? (uint32_t)(8 * q + jj) : tp;
+                    for (int jj = 0; jj < 4; ++jj) {
+                        // ids past V exist only in a ragged last tile
+                        const bool take =
+                            FULL ? (sv[jj] > tb)
+                                 : ((tv + 8u * q + 4u * khalf + jj < a.V) && (sv[jj] > tb));
+                        tb = take ? sv[jj] : tb;
+                        tp = take ? (uint32_t)(8 * q + jj) : tp;
+                    }
                 }
+                best[g] = tb;
+                bidx[g] = tp + (uint32_t)(kTileV * i);
+            } else {
+                // Tagged maximum: the sum's bf16 bits in the high half, and
+                // 31 - (position in the tile) in the low half (positions
+                // 8q + jj; the lane's 4 khalf is in first_id).  One signed
+                // integer max per logit keeps the tile's largest value and,
+                // among equal ones, the first position, for positive values;
+                // non-positive maxima are caught after the range.  The tile's
+                // maximum then meets the running one with its tag cleared, so
+                // an equal value from a later tile does not replace it.
+                int32_t m = INT32_MIN;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t s01 =
+                        add_round2(bv[q].x, round_pack2(acc[g][4 * q], acc[g][4 * q + 1]));
+                    const uint32_t s23 =
+                        add_round2(bv[q].y, round_pack2(acc[g][4 * q + 2], acc[g][4 * q + 3]));
+                    const int32_t tagged[4] = {
+                        (int32_t)((s01 << 16) | (uint32_t)(31 - 8 * q)),
+                        (int32_t)((s01 & 0xFFFF0000u) | (uint32_t)(30 - 8 * q)),
+                        (int32_t)((s23 << 16) | (uint32_t)(29 - 8 * q)),
+                        (int32_t)((s23 & 0xFFFF0000u) | (uint32_t)(28 - 8 * q))};
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        // ids past V exist only in a ragged last tile
+                        const int32_t c =
+                            FULL ? tagged[jj]
+                                 : ((tv + 8u * q + 4u * khalf + jj < a.V) ? tagged[jj]
+                                                                          : INT32_MIN);
+                        m = m > c ? m : c;
+                    }
+                }
+                const int32_t mv = (int32_t)((uint32_t)m & 0xFFFF0000u);
+                const int32_t tb = __float_as_int(best[g]);
+                const bool take = mv > tb;
+                best[g] = take ? __int_as_float(mv) : best[g];
+                bidx[g] = take ? (uint32_t)(kTileV * i) + (31u - ((uint32_t)m & 0xFFFFu))
+                               : bidx[g];
             }
-            best[g] = tb;
-            bidx[g] = tp + (uint32_t)(kTileV * i);
         }
         // tile i + 1 went out during tile i + 1 - AHEAD; only the copies of
         // the tiles after that may remain
@@ -450,17 +504,53 @@ __global__ __launch_bounds__(KW * 64) void gemm_readout_kernel(GemmArgs a)
         }
         __syncthreads();
     };
-    auto run = [&](auto ng_tag) {
+    auto run = [&](auto ng_tag, auto exact_tag) {
         int i = 0;
-        for (; i + AHEAD < Tfull; ++i) step(i, std::true_type{}, std::true_type{}, ng_tag);
-        for (; i < Tfull; ++i) step(i, std::true_type{}, std::false_type{}, ng_tag);
-        if (Tfull < T) step(T - 1, std::false_type{}, std::false_type{}, ng_tag);
+        for (; i + AHEAD < Tfull; ++i)
+            step(i, std::true_type{}, std::true_type{}, ng_tag, exact_tag);
+        for (; i < Tfull; ++i) step(i, std::true_type{}, std::false_type{}, ng_tag, exact_tag);
+        if (Tfull < T) step(T - 1, std::false_type{}, std::false_type{}, ng_tag, exact_tag);
     };
-    // both paths pass the same barriers, one per tile
+    // both paths pass the same barriers, one per tile.  The tagged epilogue
+    // serves the 8-wave shape, where the epilogue's vector work bounds the
+    // tile; the smaller shapes stream far more bytes per logit, and there the
+    // second loop the tagged epilogue needs made the kernel slower (more
+    // registers, measured 18.6 -> 29.4 us at 15 rows), so they keep the
+    // compare-and-select epilogue alone.
+    constexpr bool kTagged = (KW == kWavesMax);
     if (g1) {
-        run(std::integral_constant<int, 2>{});
+        run(std::integral_constant<int, 2>{}, std::bool_constant<!kTagged>{});
     } else {
-        run(std::integral_constant<int, 1>{});
+        run(std::integral_constant<int, 1>{}, std::bool_constant<!kTagged>{});
+    }
+    // The tagged maximum is exact where a lane's maximum is positive (bit
+    // pattern above +0).  Otherwise the whole workgroup covers its range once
+    // more with the exact epilogue: the copies of tiles 0 .. AHEAD - 1 go out
+    // again in the loop's order (x is still in registers) and every wave
+    // passes the same barriers.  Every copy of the first run has landed and
+    // been read before its last barrier.
+    if constexpr (kTagged) {
+        bool redo = false;
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+            redo |= row_ok[g] && bidx[g] != kNoIndex && __float_as_int(best[g]) <= 0;
+        if (__syncthreads_or(redo)) {
+            reset_best();
+            issue_w(-AHEAD);
+            issue_base(-AHEAD);
+            int later2 = 0;
+            for (int j = 1 - AHEAD; j < 0; ++j) {
+                issue(j);
+                later2 += n_copies(j);
+            }
+            wait_vmcnt_dyn<kMaxCount>(later2);
+            __syncthreads();
+            if (g1) {
+                run(std::integral_constant<int, 2>{}, std::true_type{});
+            } else {
+                run(std::integral_constant<int, 1>{}, std::true_type{});
+            }
+        }
     }
 
 #pragma unroll
