@@ -188,7 +188,9 @@ def test_gemm_special_values(R):
 @pytest.mark.parametrize("N,B,R", [(3, 8, 256),     # 21 rows: one wave per workgroup
                                    (10, 10, 64),    # 90 rows: two waves
                                    (20, 16, 256),   # 300 rows: eight waves
-                                   (20, 16, 128)])
+                                   (20, 16, 128),
+                                   (20, 16, 64),
+                                   (40, 16, 256)])  # 600 rows: two workgroups per range
 def test_gemm_non_positive_maxima(N, B, R):
     """Rows whose maximum is not positive, beside rows whose maximum is, in
     every launch shape: all-negative rows full of ties, rows whose maximum
