@@ -187,6 +187,7 @@ def test_gemm_special_values(R):
 
 @pytest.mark.parametrize("N,B,R", [(3, 8, 256),     # 21 rows: one wave per workgroup
                                    (10, 10, 64),    # 90 rows: two waves
+                                   (8, 16, 256),    # 120 rows: two waves
                                    (20, 16, 256),   # 300 rows: eight waves
                                    (20, 16, 128),
                                    (20, 16, 64),

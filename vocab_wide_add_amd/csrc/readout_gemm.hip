@@ -35,15 +35,16 @@
 //   * the workgroups that cover the row groups of one vocabulary range are
 //     placed on one XCD (workgroup b runs on XCD b mod 8), so each w tile is
 //     fetched from HBM once and served from that XCD's L2 afterwards;
-//   * in the 8-wave shape the epilogue keeps a tile's first maximum in one
-//     integer max per logit: a widened bf16 sum has 16 zero low bits, which
-//     take a tag that falls with the id's position in the tile, so among
-//     equal values the earlier id has the larger bit pattern; the running
-//     (value, id) is updated once per tile.  For positive values the bit patterns order as
-//     the values do (+inf included), so this is exact wherever a lane's
-//     maximum over its range is positive; a workgroup in which some lane's
-//     maximum is not (zero, negative, -inf) runs its range again with the
-//     per-logit compare-and-select epilogue, which is exact for every value;
+//   * in the 2- and 8-wave shapes the epilogue keeps a tile's first maximum
+//     in one integer max per logit: a widened bf16 sum has 16 zero low bits,
+//     which take a tag that falls with the id's position in the tile, so
+//     among equal values the earlier id has the larger bit pattern; the
+//     running (value, id) is updated once per tile.  For positive values the
+//     bit patterns order as the values do (+inf included), so this is exact
+//     wherever a lane's maximum over its range is positive; a workgroup in
+//     which some lane's maximum is not (zero, negative, -inf) runs its range
+//     again with the per-logit compare-and-select epilogue, which is exact
+//     for every value and is the one-wave shape's only epilogue;
 //   * per (row, range) the packed (value, ~id) key goes to a key table and the
 //     library's second pass reduces each row's keys into blk.
 // Numerics: the fp32 accumulation order of the MFMA is the hardware's; where
@@ -512,12 +513,12 @@ __global__ __launch_bounds__(KW * 64) void gemm_readout_kernel(GemmArgs a)
         if (Tfull < T) step(T - 1, std::false_type{}, std::false_type{}, ng_tag, exact_tag);
     };
     // both paths pass the same barriers, one per tile.  The tagged epilogue
-    // serves the 8-wave shape, where the epilogue's vector work bounds the
-    // tile; the smaller shapes stream far more bytes per logit, and there the
-    // second loop the tagged epilogue needs made the kernel slower (more
-    // registers, measured 18.6 -> 29.4 us at 15 rows), so they keep the
-    // compare-and-select epilogue alone.
-    constexpr bool kTagged = (KW == kWavesMax);
+    // serves the 2- and 8-wave shapes (measured: 61.0 -> 57.7 us at 480
+    // rows, 29.1 -> 28.6 us at 120 rows); in the one-wave shape, which is
+    // bound by streaming w, the second loop the tagged epilogue needs made
+    // the kernel slower (342 instead of 292 registers, 18.6 -> 29.4 us at 15
+    // rows), so it keeps the compare-and-select epilogue alone.
+    constexpr bool kTagged = (KW >= 2);
     if (g1) {
         run(std::integral_constant<int, 2>{}, std::bool_constant<!kTagged>{});
     } else {
