@@ -76,6 +76,11 @@ def _load():
             _U16P, _U16P, _U16P, _I64P] + [ctypes.c_int64] * 5
         lib.oracle_gemm_argmax_rows.restype = ctypes.c_int
         _DP = ctypes.POINTER(ctypes.c_double)
+        lib.oracle_bf16_to_double_many.argtypes = [_U16P, _DP, ctypes.c_int64]
+        lib.oracle_bf16_to_double_many.restype = None
+        lib.oracle_gemm_argmax_rows_decoded.argtypes = [
+            _U16P, _DP, _DP, _I64P] + [ctypes.c_int64] * 5
+        lib.oracle_gemm_argmax_rows_decoded.restype = ctypes.c_int
         lib.oracle_bf16_from_double_many.argtypes = [_DP, _U16P, ctypes.c_int64]
         lib.oracle_bf16_from_double_many.restype = None
         lib.oracle_latent_pass.argtypes = (
@@ -243,11 +248,22 @@ def dot_bf16(x_row, w_row) -> int:
     return int(_load().oracle_dot_bf16(_p16(a), _p16(b), a.size))
 
 
+def bf16_to_double_many(h) -> np.ndarray:
+    """binary64 values of an array of bf16 patterns (the oracle's decoding)."""
+    h = _u16(h).reshape(-1)
+    out = np.empty(h.size, dtype=np.float64)
+    _load().oracle_bf16_to_double_many(_p16(h), out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                       h.size)
+    return out
+
+
 def gemm_argmax_rows(base, x, w, rows, V: int, R: int, stride_base_r: int,
                      threads: int = 1) -> np.ndarray:
     """First argmax of bf16(base + bf16(x @ w.T)) for each row listed in
     ``rows`` (an iterable of row indices); base [.., stride], x [.., R] and
-    w [V, R] are uint16 bf16 patterns.  Rows are spread over host threads."""
+    w [V, R] are uint16 bf16 patterns.  x and w are decoded to binary64 once
+    (``oracle_gemm_argmax_rows_decoded``: the same arithmetic as
+    ``oracle_gemm_argmax_rows``); rows are spread over host threads."""
     base = _u16(base).reshape(-1)
     x = _u16(x).reshape(-1)
     w = _u16(w).reshape(-1)
@@ -258,20 +274,26 @@ def gemm_argmax_rows(base, x, w, rows, V: int, R: int, stride_base_r: int,
         if r < 0 or (r + 1) * R > x.size or r * stride_base_r + V > base.size:
             raise ValueError("row %d outside the buffers" % r)
     out = np.empty(len(rows), dtype=np.int64)
+    if not rows:
+        return out
     lib = _load()
+    dp = ctypes.POINTER(ctypes.c_double)
+    wd = bf16_to_double_many(w[:V * R])
+    xd = bf16_to_double_many(x[:(max(rows) + 1) * R])
 
     def work(idx):
         one = np.empty(1, dtype=np.int64)
         for j in idx:
             r = rows[j]
-            rc = lib.oracle_gemm_argmax_rows(_p16(base), _p16(x), _p16(w),
-                                             one.ctypes.data_as(_I64P), r, r + 1, V, R,
-                                             stride_base_r)
+            rc = lib.oracle_gemm_argmax_rows_decoded(_p16(base), xd.ctypes.data_as(dp),
+                                                     wd.ctypes.data_as(dp),
+                                                     one.ctypes.data_as(_I64P), r, r + 1, V, R,
+                                                     stride_base_r)
             if rc != 0:
                 raise ValueError("oracle rejected the sizes")
             out[j] = one[0]
 
-    threads = max(1, min(int(threads), len(rows) if rows else 1))
+    threads = max(1, min(int(threads), len(rows)))
     parts = [list(range(t, len(rows), threads)) for t in range(threads)]
     ts = [threading.Thread(target=work, args=(p,)) for p in parts]
     for t in ts:

@@ -30,7 +30,9 @@
  *   - on equal maxima the lowest vocabulary index wins (what an argmax over
  *     the chunk followed by a strict ">" scan over chunks in ascending order
  *     yields);
- *   - NaN inputs are outside the contract; a NaN sum never wins here.
+ *   - NaN inputs are outside the contract; a NaN sum never wins here, at any
+ *     position: the scan starts from -inf at index 0 and takes only a
+ *     strictly greater value, so a row of NaN and -inf sums reports index 0.
  *
  * Everything is single-threaded and unvectorised on purpose.
  */
@@ -127,7 +129,6 @@ uint16_t oracle_bf16_from_double(double x)
     return sign | (uint16_t)(efield << 7) | (uint16_t)((int)m - 128);
 }
 
-/* The rounded sum of one pair: bf16(a + b), formed in binary64. */
 /* Element-wise oracle_bf16_from_double over n values. */
 void oracle_bf16_from_double_many(const double* x, uint16_t* out, int64_t n)
 {
@@ -136,6 +137,7 @@ void oracle_bf16_from_double_many(const double* x, uint16_t* out, int64_t n)
     }
 }
 
+/* The rounded sum of one pair: bf16(a + b), formed in binary64. */
 uint16_t oracle_bf16_sum(uint16_t a, uint16_t b)
 {
     double s = oracle_bf16_to_double(a) + oracle_bf16_to_double(b);
@@ -163,14 +165,15 @@ void oracle_bf16_sum_grid(const uint16_t* a_vals, int64_t n_a, uint16_t* out)
 }
 
 /* Argmax of one row: the lowest v whose rounded sum equals the row maximum.
- * The scan runs v = 0 .. V-1 and replaces the incumbent only on a strictly
- * greater value, which is exactly "first maximum".  V >= 1. */
+ * The scan runs v = 0 .. V-1 from the incumbent (-inf, index 0) and replaces
+ * it only on a strictly greater value, which is exactly "first maximum"; a
+ * NaN sum compares false and never replaces it.  V >= 1. */
 int64_t oracle_add_argmax_row(const uint16_t* base_row, const uint16_t* bias_row,
                               int64_t V)
 {
     int64_t best_v = 0;
-    double best = oracle_bf16_to_double(oracle_bf16_sum(base_row[0], bias_row[0]));
-    for (int64_t v = 1; v < V; ++v) {
+    double best = -INFINITY;
+    for (int64_t v = 0; v < V; ++v) {
         double s = oracle_bf16_to_double(oracle_bf16_sum(base_row[v], bias_row[v]));
         if (s > best) {
             best = s;
@@ -273,24 +276,62 @@ uint16_t oracle_dot_bf16(const uint16_t* x_row, const uint16_t* w_row, int64_t R
     return oracle_bf16_from_double(acc);
 }
 
-/* First argmax of bf16(base + bf16(x_row . w[v])) over v = 0 .. V-1. */
-int64_t oracle_gemm_argmax_row(const uint16_t* base_row, const uint16_t* x_row,
-                               const uint16_t* w, int64_t V, int64_t R)
+/* Element-wise bf16 decoding of n patterns into binary64. */
+void oracle_bf16_to_double_many(const uint16_t* h, double* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        out[i] = oracle_bf16_to_double(h[i]);
+    }
+}
+
+/* First argmax of bf16(base + bf16(x_row . w[v])) over v = 0 .. V-1, with
+ * x_row [R] and w [V, R] given decoded to binary64 (oracle_bf16_to_double:
+ * every bf16 value is exact there, so decoding once is a change of storage,
+ * not of the arithmetic).  Each product of two bf16 values is exact in
+ * binary64; the sum over k runs in order k = 0 .. R-1 and is rounded once
+ * to bf16 (the matmul's bf16 output), then added to base and rounded again.
+ * The incumbent starts at (-inf, index 0) and only a strictly greater value
+ * replaces it, as in the readout above. */
+static int64_t gemm_scan_row(const uint16_t* base_row, const double* x_row,
+                             const double* w, int64_t V, int64_t R)
 {
     int64_t best_v = 0;
-    double best = 0.0;
+    double best = -INFINITY;
     for (int64_t v = 0; v < V; ++v) {
-        uint16_t bias = oracle_dot_bf16(x_row, w + v * R, R);
-        double s = oracle_bf16_to_double(oracle_bf16_sum(base_row[v], bias));
-        if (v == 0 || s > best) {
-            best = s;
+        const double* wv = w + v * R;
+        double acc = 0.0;
+        for (int64_t k = 0; k < R; ++k) {
+            acc += x_row[k] * wv[k];
+        }
+        uint16_t bias = oracle_bf16_from_double(acc);
+        double sum = oracle_bf16_to_double(oracle_bf16_sum(base_row[v], bias));
+        if (sum > best) {
+            best = sum;
             best_v = v;
         }
     }
     return best_v;
 }
 
-/* Rows [r0, r1): idx_out[r - r0] = first argmax of row r. */
+/* Rows [r0, r1) on decoded operands: xd [rows, R] and wd [V, R] binary64
+ * (oracle_bf16_to_double_many of x and w); idx_out[r - r0] = first argmax
+ * of row r. */
+int oracle_gemm_argmax_rows_decoded(const uint16_t* base, const double* xd, const double* wd,
+                                    int64_t* idx_out, int64_t r0, int64_t r1, int64_t V,
+                                    int64_t R, int64_t stride_base_r)
+{
+    if (r0 < 0 || r1 < r0 || V < 1 || R < 1 || stride_base_r < V) {
+        return -1;
+    }
+    for (int64_t r = r0; r < r1; ++r) {
+        idx_out[r - r0] = gemm_scan_row(base + r * stride_base_r, xd + r * R, wd, V, R);
+    }
+    return 0;
+}
+
+/* Rows [r0, r1) on bf16 operands: decodes x's rows r0 .. r1-1 and all of w,
+ * then scans each row.  Returns 0, -1 on invalid sizes, -2 when out of host
+ * memory. */
 int oracle_gemm_argmax_rows(const uint16_t* base, const uint16_t* x, const uint16_t* w,
                             int64_t* idx_out, int64_t r0, int64_t r1, int64_t V,
                             int64_t R, int64_t stride_base_r)
@@ -298,10 +339,20 @@ int oracle_gemm_argmax_rows(const uint16_t* base, const uint16_t* x, const uint1
     if (r0 < 0 || r1 < r0 || V < 1 || R < 1 || stride_base_r < V) {
         return -1;
     }
-    for (int64_t r = r0; r < r1; ++r) {
-        idx_out[r - r0] = oracle_gemm_argmax_row(base + r * stride_base_r, x + r * R, w, V, R);
+    double* wd = (double*)malloc(sizeof(double) * (size_t)(V * R));
+    double* xd = (double*)malloc(sizeof(double) * (size_t)((r1 - r0) * R + 1));
+    if (!wd || !xd) {
+        free(wd);
+        free(xd);
+        return -2;
     }
-    return 0;
+    oracle_bf16_to_double_many(w, wd, V * R);
+    oracle_bf16_to_double_many(x + r0 * R, xd, (r1 - r0) * R);
+    int rc = oracle_gemm_argmax_rows_decoded(base + r0 * stride_base_r, xd, wd, idx_out, 0,
+                                             r1 - r0, V, R, stride_base_r);
+    free(wd);
+    free(xd);
+    return rc;
 }
 
 /* ---------------------------------------------------------------------------

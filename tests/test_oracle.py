@@ -41,9 +41,9 @@ def load_rounding_cases():
     return out
 
 
-def load_argmax_rows():
+def load_argmax_rows(fname="argmax_rows.txt"):
     out = []
-    with open(os.path.join(GOLDEN, "argmax_rows.txt")) as f:
+    with open(os.path.join(GOLDEN, fname)) as f:
         for line in f:
             line = line.strip()
             if not line or line.startswith("#"):
@@ -57,6 +57,7 @@ def load_argmax_rows():
 
 ROUNDING = load_rounding_cases()
 ARGMAX_ROWS = load_argmax_rows()
+NAN_ROWS = load_argmax_rows("nan_rows.txt")
 
 
 @pytest.mark.parametrize("a,b,expected,why", ROUNDING,
@@ -73,6 +74,20 @@ def test_rounding_golden(a, b, expected, why):
 def test_argmax_golden(name, base, bias, idx, why):
     assert oracle.add_argmax_row(base, bias) == idx, why
     assert exact_bf16.first_argmax(base, bias) == idx, why
+
+
+@pytest.mark.parametrize("name,base,bias,idx,why", NAN_ROWS, ids=[c[0] for c in NAN_ROWS])
+def test_nan_rows_golden(name, base, bias, idx, why):
+    """NaN sums (outside the contract; the pages are silent): the reading
+    taken is that a NaN sum never wins, at any position, so the first maximum
+    of the other sums wins, and a row of NaN and -inf sums gives index 0."""
+    assert oracle.add_argmax_row(base, bias) == idx, why
+    # the same rows through the top-C readout (ids = 100 + position)
+    C = base.size
+    cand = np.arange(100, 100 + C, dtype=np.int64)
+    blk = np.array([[-5, -1]], dtype=np.int64)
+    oracle.topc_argmax_to_blk(base, bias, cand, blk, 1, 2, C)
+    assert blk[0, 0] == -5 and blk[0, 1] == 100 + idx, why
 
 
 def test_decode_closed_forms():

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import exact_bf16
-from test_oracle import ARGMAX_ROWS, GEMM_ROWS, ROUNDING, TOPC_ROWS
+from test_oracle import ARGMAX_ROWS, GEMM_ROWS, NAN_ROWS, ROUNDING, TOPC_ROWS
 from test_oracle_latent import latent_pins_pass
 from vocab_wide_add_amd import workloads
 
@@ -45,11 +45,14 @@ MUTATIONS = {
                              "blk[n * B + 1 + j] = best;"),
     "topc_wrong_row": ("blk[n * B + 1 + j] = cand[r * C + best];",
                        "blk[n * B + 1 + j] = cand[best];"),
+    "nan_at_first_index_wins": ("if (s > best) {", "if (s > best || v == 0) {"),
     "gemm_bias_dropped": ("oracle_bf16_sum(base_row[v], bias)", "oracle_bf16_sum(base_row[v], 0)"),
-    "gemm_x_row_ignored": ("oracle_gemm_argmax_row(base + r * stride_base_r, x + r * R, w, V, R)",
-                           "oracle_gemm_argmax_row(base + r * stride_base_r, x, w, V, R)"),
-    "gemm_bias_unrounded": ("return oracle_bf16_from_double(acc);",
-                            "return oracle_bf16_from_double(acc) | 1;"),
+    "gemm_x_row_ignored": ("gemm_scan_row(base + r * stride_base_r, xd + r * R, wd, V, R)",
+                           "gemm_scan_row(base + r * stride_base_r, xd, wd, V, R)"),
+    "gemm_bias_unrounded": ("uint16_t bias = oracle_bf16_from_double(acc);",
+                            "uint16_t bias = oracle_bf16_from_double(acc) | 1;"),
+    "gemm_last_max_wins": ("if (sum > best) {", "if (sum >= best) {"),
+    "gemm_w_row_stride": ("const double* wv = w + v * R;", "const double* wv = w + v;"),
     # latent stage
     "latent_prev_is_same_slot": ("int64_t tok = (b == 0) ? am1[n] : blk[n * B + b - 1];",
                                  "int64_t tok = (b == 0) ? am1[n] : blk[n * B + b];"),
@@ -134,7 +137,7 @@ def _pins_pass(lib) -> bool:
     for a, b, e, _ in ROUNDING:
         if lib.oracle_bf16_sum(a, b) != e:
             return False
-    for _, base, bias, idx, _ in ARGMAX_ROWS:
+    for _, base, bias, idx, _ in ARGMAX_ROWS + NAN_ROWS:
         base = np.ascontiguousarray(base)
         bias = np.ascontiguousarray(bias)
         if lib.oracle_add_argmax_row(base.ctypes.data_as(U16P), bias.ctypes.data_as(U16P),
