@@ -78,6 +78,11 @@ extern "C" {
  * one per (device, stream), allocated on first use and left zeroed by every
  * call, so repeated calls and graph replays need no clearing.  Calls queued
  * on different streams use different workspaces and may run concurrently.
+ * When a later call needs more, the workspace grows (synchronously, outside
+ * capture only) into a new allocation and the old one is retired, not freed:
+ * queued work and HIP graphs captured before keep valid memory until
+ * xpress_release.  The same rules hold for every entry point below that
+ * uses the workspace.
  * The caller keeps every buffer alive until the queued work has finished.
  * Host threads: the library's own tables are locked, but a call holds its
  * stream's workspace from lookup to launch, so calls that queue on one
@@ -148,7 +153,9 @@ int xpress_topc_argmax_to_blk(const uint16_t* base_c, const uint16_t* bias_c,
  * rows x 512 x 8 bytes), grown on first use.  xpress_reserve does not size
  * it: before capturing this call into a HIP graph, make one call with at
  * least as many rows on the same stream outside capture (a capture that
- * would have to grow it returns XPRESS_ECAPTURE).
+ * would have to grow it returns XPRESS_ECAPTURE and queues nothing).  Later
+ * growth retires the old table rather than freeing it, so graphs captured
+ * earlier stay valid until xpress_release.
  */
 int xpress_readout_gemm_argmax_to_blk(const uint16_t* base, const uint16_t* x,
                                       const uint16_t* w, int64_t* blk, int64_t N,
@@ -208,7 +215,8 @@ int xpress_reserve(int64_t N, int64_t B, int64_t V, hipStream_t stream);
  * Asynchronous; three launches on `stream`.  N == 0 queues nothing.  Uses the
  * (device, stream) workspace for u, bf16(u) and m (rows * (6R + 2H) bytes,
  * rows = N * (B-1)); grow it beforehand with xpress_latent_reserve when the
- * call will be captured into a HIP graph.  Errors: XPRESS_EINVAL (sizes,
+ * call will be captured into a HIP graph (growth retires the old regions
+ * rather than freeing them, as for the readouts).  Errors: XPRESS_EINVAL (sizes,
  * alignment, null pointers, overlap; nothing queued), XPRESS_ENOMEM /
  * XPRESS_ECAPTURE (workspace), XPRESS_EHIP (launch).
  */
@@ -223,7 +231,8 @@ int xpress_latent_pass(const int64_t* blk, const int64_t* am1, const uint16_t* x
  * xpress_latent_pass needs for (N, B, R, H), so that a captured call
  * allocates nothing.  Synchronous.  Returns XPRESS_OK, XPRESS_EINVAL,
  * XPRESS_ENOMEM or XPRESS_EHIP.  Growing the workspace later (a larger shape
- * on the same stream) invalidates graphs captured before.
+ * on the same stream) retires the old regions, which graphs captured before
+ * keep using until xpress_release.
  */
 int xpress_latent_reserve(int64_t N, int64_t B, int64_t R, int64_t H, hipStream_t stream);
 
@@ -245,12 +254,29 @@ int xpress_latent_set_tiles(int mix, int gate, int down);
 
 /*
  * xpress_release -- free every workspace the library holds on the current
- * device (after synchronising that device).  Optional; for tests and for
- * callers that want the memory back.  No other call of the library may be in
- * progress meanwhile, and graphs captured before hold freed workspace and
- * must not be replayed; the next call allocates afresh.
+ * device, live and retired (after synchronising that device).  Optional; for
+ * tests and for callers that want the memory back.  No other call of the
+ * library may be in progress meanwhile, and graphs captured before hold freed
+ * workspace and must not be replayed; the next call allocates afresh.
  */
 int xpress_release(void);
+
+/*
+ * xpress_set_workspace_limit -- cap, in bytes, on the workspace (live plus
+ * retired) the library may hold per device; 0 (the default) means no cap.
+ * A call whose workspace would have to grow past the cap returns
+ * XPRESS_ENOMEM and queues nothing, exactly as when the device is out of
+ * memory.  Process-wide.  Returns XPRESS_OK, or XPRESS_EINVAL for a negative
+ * cap.
+ */
+int xpress_set_workspace_limit(int64_t bytes);
+
+/*
+ * xpress_workspace_bytes -- *live_and_retired = the bytes of workspace the
+ * library holds on the current device.  Returns XPRESS_OK, XPRESS_EINVAL
+ * (null pointer) or XPRESS_EHIP.
+ */
+int xpress_workspace_bytes(int64_t* live_and_retired);
 
 /*
  * Plan override, for tests and tuning.  combine selects how a row's partial
@@ -293,6 +319,18 @@ int xpress_describe_plan(const uint16_t* base, const uint16_t* bias, int64_t N,
                          int64_t B, int64_t V, int64_t stride_base_r,
                          int64_t stride_bias_r, int* combine, int* splits,
                          int* block_threads, int* vector_path, int* launches);
+
+/*
+ * xpress_describe_gemm_plan -- the launch shape xpress_readout_gemm_argmax_to_blk
+ * would use for (N, B, V): *waves per workgroup (1, 2 or 8; each wave holds
+ * 64 draft rows), *ranges (the vocabulary is cut into this many contiguous
+ * ranges of whole 32-id tiles, a multiple of 8), *row_wgs (workgroups per
+ * range) and *tiles (ceil(V / 32)).  Any output may be null.  Pure host
+ * computation on the current device's compute-unit count.  Returns
+ * XPRESS_OK or XPRESS_EINVAL.
+ */
+int xpress_describe_gemm_plan(int64_t N, int64_t B, int64_t V, int* waves, int* ranges,
+                              int* row_wgs, int* tiles);
 
 /*
  * xpress_bf16_add_round_table -- the readout's element step alone, for

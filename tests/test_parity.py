@@ -436,3 +436,29 @@ def test_balanced_ties_on_range_edges(per_cu, threads):
         for _ in range(3):
             got = gpu_blk(bd, id_, blk0, N, B, V, S, S)
             assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("combine", COMBINES)
+def test_nan_sums_never_win(combine):
+    """NaN sums are outside the contract; the reading taken (the oracle's) is
+    that a NaN never wins: NaN at index 0, NaN beside +inf, +inf + -inf,
+    NaN with the sign set, and a row of NaN and -inf sums (index 0)."""
+    V = 5000
+    a = np.zeros((6, V), dtype=np.uint16)
+    b = np.zeros((6, V), dtype=np.uint16)
+    a[0, 0] = 0x7FC0; a[0, 4000] = 0x3F80                       # NaN first, 1 later
+    a[1, :] = 0xBF80; a[1, 3] = 0x7F80; b[1, 3] = 0xFF80       # +inf + -inf, rest -1
+    a[1, 4500] = 0x3F00
+    a[2, 10] = 0x7FC0; a[2, 11] = 0x7F80; a[2, 4999] = 0x7F80  # NaN before +inf
+    a[3, :] = 0xFF80; a[3, 7] = 0xFFC0; a[3, 4097] = 0x7FC0    # -inf and NaN only
+    a[4, 100] = 0xFFC0; a[4, 4096] = 0x3F80; a[4, 4097] = 0x3F80
+    a[5, :] = 0x7FC1                                            # every sum NaN
+    N, B = 6, 2
+    blk0 = np.full((N, B), 4, dtype=np.int64)
+    want = oracle_blk(a, b, blk0, N, B, V, V, V)
+    assert list(want[:, 1]) == [4000, 4500, 11, 0, 4096, 0]
+    for splits in (1, 2, 5):
+        say("NaN rows combine=%d splits=%d" % (combine, splits))
+        with Plan(combine, splits, 64):
+            got = gpu_blk(to_dev(a), to_dev(b), blk0, N, B, V, V, V)
+        assert np.array_equal(got, want), splits

@@ -220,7 +220,7 @@ def test_gemm_non_positive_maxima(N, B, R):
             base[r, zpos[3:]] = 0
         elif k == 3:     # -inf everywhere but one negative value
             base[r, :] = NEG_INF
-            base[r, g.integers(0, V)] = workloads.f32_to_bf16_bits(np.float32(-3.0))
+            base[r, g.integers(0, V)] = workloads.f32_to_bf16_bits(np.array([-3.0], np.float32))[0]
         elif k == 4:     # negative over the first part, positive after
             cut = int(g.integers(V // 4, 3 * V // 4))
             x[r, :] = 0

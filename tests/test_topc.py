@@ -187,3 +187,32 @@ def test_topc_special_values(C):
     say("topc special values C=%d" % C)
     got = gpu_topc(to_dev(base_c), to_dev(bias_c), to_dev(cand), blk0, N, B, C)
     assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("C", [64, 256, 1024])    # one wave per row up to 256, else streaming
+def test_topc_nan_sums_never_win(C):
+    """A NaN sum never wins on either top-C path (the oracle's reading of a
+    case outside the contract): NaN at position 0 of every lane, NaN from
+    +inf + -inf before +inf, NaN with the sign set, and rows whose sums are
+    all NaN or NaN and -inf (position 0's id)."""
+    N, B = 2, 5
+    rows = N * (B - 1)
+    g = np.random.Generator(np.random.PCG64(6060 + C))
+    base_c = workloads.f32_to_bf16_bits((g.integers(-8, 9, size=(rows, C)) / 4.0).astype(np.float32))
+    bias_c = np.zeros((rows, C), dtype=np.uint16)
+    cand = (g.permutation(rows * C).astype(np.int64).reshape(rows, C) + (1 << 34))
+    base_c[0, :64] = 0x7FC0                       # each lane's first candidate is NaN
+    base_c[1, 5] = 0x7F80; bias_c[1, 5] = 0xFF80  # +inf + -inf = NaN ...
+    base_c[1, C - 1] = 0x7F80                     # ... before the only +inf
+    base_c[2, ::3] = 0xFFC0                       # NaN with the sign set
+    base_c[3, :] = 0x7FC0                         # every sum NaN: position 0
+    base_c[4, :] = 0xFF80
+    base_c[4, 1::2] = 0x7FC0                      # -inf and NaN: position 0
+    blk0 = np.full((N, B), -1, dtype=np.int64)
+    blk0[:, 0] = 12
+    want = oracle_topc(base_c, bias_c, cand, blk0, N, B, C)
+    w1 = want[:, 1:].reshape(-1)
+    assert w1[1] == cand[1, C - 1] and w1[3] == cand[3, 0] and w1[4] == cand[4, 0]
+    say("topc NaN sums C=%d" % C)
+    got = gpu_topc(to_dev(base_c), to_dev(bias_c), to_dev(cand), blk0, N, B, C)
+    assert np.array_equal(got, want)

@@ -524,8 +524,10 @@ __global__ __launch_bounds__(KW * 64) void gemm_readout_kernel(GemmArgs a)
     } else {
         run(std::integral_constant<int, 1>{}, std::bool_constant<!kTagged>{});
     }
-    // The tagged maximum is exact where a lane's maximum is positive (bit
-    // pattern above +0).  Otherwise the whole workgroup covers its range once
+    // The tagged maximum is exact where a lane's maximum is positive and not
+    // NaN (bit pattern above +0, at most +inf's).  A positive NaN sum has the
+    // largest bit pattern of all and would win, where the compare-and-select
+    // epilogue never takes a NaN.  Otherwise the whole workgroup covers its range once
     // more with the exact epilogue: the copies of tiles 0 .. AHEAD - 1 go out
     // again in the loop's order (x is still in registers) and every wave
     // passes the same barriers.  Every copy of the first run has landed and
@@ -534,7 +536,8 @@ __global__ __launch_bounds__(KW * 64) void gemm_readout_kernel(GemmArgs a)
         bool redo = false;
 #pragma unroll
         for (int g = 0; g < kGroups; ++g)
-            redo |= row_ok[g] && bidx[g] != kNoIndex && __float_as_int(best[g]) <= 0;
+            redo |= row_ok[g] && bidx[g] != kNoIndex &&
+                    (__float_as_int(best[g]) <= 0 || __float_as_int(best[g]) > 0x7F800000);
         if (__syncthreads_or(redo)) {
             reset_best();
             issue_w(-AHEAD);
@@ -585,7 +588,53 @@ hipError_t launch_gemm(const GemmArgs& a, int waves, uint32_t grid, hipStream_t 
     return hipGetLastError();
 }
 
+// Launch shape for `rows` draft rows over V ids.  Up to 64 rows: one wave
+// per workgroup, up to 128: two (two workgroups per CU either way, LDS
+// allowing); beyond: eight waves (512 rows), one workgroup per CU, and as
+// many workgroups per range as the rows need.  The vocabulary is cut into a
+// multiple of 8 ranges (one per XCD slot) of whole 32-id tiles.  Returns
+// false when the grid would not fit 31 bits.
+struct GemmPlan {
+    int waves;
+    uint32_t tiles;
+    uint32_t row_wgs;
+    uint32_t ranges;
+};
+
+bool gemm_plan(int64_t rows, int64_t V, GemmPlan* p)
+{
+    p->tiles = (uint32_t)((V + kTileV - 1) / kTileV);
+    p->waves = rows <= 64 ? 1 : rows <= 128 ? 2 : kWavesMax;
+    const int per_cu = p->waves == kWavesMax ? 1 : 2;
+    const int64_t rows_per_wg = (int64_t)p->waves * 32 * kGroups;
+    const int64_t row_wgs = (rows + rows_per_wg - 1) / rows_per_wg;
+    int64_t ranges = (int64_t)device_cus() * per_cu / row_wgs;
+    ranges = ranges / 8 * 8;
+    if (ranges < 8) ranges = 8;
+    const int64_t max_ranges = ((int64_t)p->tiles + 7) / 8 * 8;
+    if (ranges > max_ranges) ranges = max_ranges;
+    if (row_wgs * ranges > 0x7FFFFFFFll) return false;
+    p->row_wgs = (uint32_t)row_wgs;
+    p->ranges = (uint32_t)ranges;
+    return true;
+}
+
 }  // namespace
+
+extern "C" int xpress_describe_gemm_plan(int64_t N, int64_t B, int64_t V, int* waves,
+                                         int* ranges, int* row_wgs, int* tiles)
+{
+    if (N < 0 || B < 1 || V < 1 || V > 0x7FFFFFFFll) return XPRESS_EINVAL;
+    if (B - 1 > 0 && N > 0x7FFFFFFFll / (B - 1)) return XPRESS_EINVAL;
+    const int64_t rows = N * (B - 1);
+    GemmPlan p;
+    if (!gemm_plan(rows > 0 ? rows : 1, V, &p)) return XPRESS_EINVAL;
+    if (waves) *waves = p.waves;
+    if (ranges) *ranges = (int)p.ranges;
+    if (row_wgs) *row_wgs = (int)p.row_wgs;
+    if (tiles) *tiles = (int)p.tiles;
+    return XPRESS_OK;
+}
 
 extern "C" int xpress_readout_gemm_argmax_to_blk(const uint16_t* base, const uint16_t* x,
                                                  const uint16_t* w, int64_t* blk, int64_t N,
@@ -612,6 +661,8 @@ extern "C" int xpress_readout_gemm_argmax_to_blk(const uint16_t* base, const uin
         return XPRESS_EINVAL;
     }
 
+    GemmPlan p;
+    if (!gemm_plan(rows, V, &p)) return XPRESS_EINVAL;
     GemmArgs a;
     a.base = base;
     a.x = x;
@@ -619,32 +670,19 @@ extern "C" int xpress_readout_gemm_argmax_to_blk(const uint16_t* base, const uin
     a.stride_base = stride_base_r;
     a.rows = (uint32_t)rows;
     a.V = (uint32_t)V;
-    a.tiles = (uint32_t)((V + kTileV - 1) / kTileV);
-    // Up to 64 rows: one wave per workgroup, up to 128: two (two workgroups
-    // per CU either way, LDS allowing); beyond: eight waves (512 rows), one
-    // workgroup per CU, and as many workgroups per range as the rows need.
-    const int waves = rows <= 64 ? 1 : rows <= 128 ? 2 : kWavesMax;
-    const int per_cu = waves == kWavesMax ? 1 : 2;
-    const int64_t rows_per_wg = (int64_t)waves * 32 * kGroups;
-    a.row_wgs = (uint32_t)((rows + rows_per_wg - 1) / rows_per_wg);
-    // ranges a multiple of 8 (one per XCD slot)
-    int64_t ranges = (int64_t)device_cus() * per_cu / a.row_wgs;
-    ranges = ranges / 8 * 8;
-    if (ranges < 8) ranges = 8;
-    const int64_t max_ranges = ((int64_t)a.tiles + 7) / 8 * 8;
-    if (ranges > max_ranges) ranges = max_ranges;
-    if ((int64_t)a.row_wgs * ranges > 0x7FFFFFFFll) return XPRESS_EINVAL;
-    a.ranges = (uint32_t)ranges;
+    a.tiles = p.tiles;
+    a.row_wgs = p.row_wgs;
+    a.ranges = p.ranges;
 
-    int rc = workspace_table(stream, rows * ranges, &a.table);
+    int rc = workspace_table(stream, rows * (int64_t)p.ranges, &a.table);
     if (rc != XPRESS_OK) return rc;
 
     const uint32_t grid = a.row_wgs * a.ranges;
     hipError_t e;
     switch (R) {
-        case 64: e = launch_gemm<64>(a, waves, grid, stream); break;
-        case 128: e = launch_gemm<128>(a, waves, grid, stream); break;
-        default: e = launch_gemm<256>(a, waves, grid, stream); break;
+        case 64: e = launch_gemm<64>(a, p.waves, grid, stream); break;
+        case 128: e = launch_gemm<128>(a, p.waves, grid, stream); break;
+        default: e = launch_gemm<256>(a, p.waves, grid, stream); break;
     }
     if (e != hipSuccess) return hip_fail(e);
     e = launch_reduce_table(a.table, blk, nullptr, a.rows, (uint32_t)(B - 1), a.V, a.ranges,

@@ -41,6 +41,7 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "xpress_argmax.h"
 #include "device_common.h"
@@ -311,8 +312,10 @@ __global__ __launch_bounds__(T) void readout_balanced_kernel(RowArgs a)
 // so after the wave's (value, position) reduction the lane that holds the
 // winning position writes its id -- no second, dependent memory round trip
 // for the gather.  A lane replaces its incumbent only on a strictly larger
-// value (or when it has none yet), visiting its positions in ascending
-// order, so it keeps its first maximum.
+// value (or, when it has none yet, on any value but NaN), visiting its
+// positions in ascending order, so it keeps its first maximum and never
+// holds a NaN.  A row whose sums are all NaN (no lane holds a candidate)
+// writes its first candidate's id, as a row of -inf sums does.
 template <bool VEC>
 __global__ __launch_bounds__(256) void topc_wave_kernel(const uint16_t* __restrict__ base_c,
                                                         const uint16_t* __restrict__ bias_c,
@@ -331,7 +334,7 @@ __global__ __launch_bounds__(256) void topc_wave_kernel(const uint16_t* __restri
         uint32_t bi = kNoIndex;
         int64_t bid = 0;
         auto take = [&](float sv, uint32_t c, int64_t id) {
-            const bool t = (sv > best) | (bi == kNoIndex);
+            const bool t = (sv > best) | ((bi == kNoIndex) & (sv == sv));
             best = t ? sv : best;
             bi = t ? c : bi;
             bid = t ? id : bid;
@@ -365,9 +368,12 @@ __global__ __launch_bounds__(256) void topc_wave_kernel(const uint16_t* __restri
         float v = best;
         uint32_t i = bi;
         wave_argmax(v, i);
-        if (bi == i && i != kNoIndex) {
-            const uint32_t n = row / bm1;
-            blk[(int64_t)n * (bm1 + 1) + 1 + (row - n * bm1)] = bid;
+        const uint32_t n = row / bm1;
+        int64_t* slot = blk + (int64_t)n * (bm1 + 1) + 1 + (row - n * bm1);
+        if (i == kNoIndex) {
+            if (lane == 0u) *slot = cd[0];
+        } else if (bi == i) {
+            *slot = bid;
         }
     }
 }
@@ -557,7 +563,11 @@ Plan make_plan(const uint16_t* base, const uint16_t* bias, int64_t rows, int64_t
 // Per (device, stream) workspace.  The atomic region ([rows] u64
 // key-and-count words) is zero when idle: allocated zeroed, and every call's
 // last arriver clears the word it used.  The table region is overwritten
-// whole by every two-pass call.
+// whole by every two-pass call.  A region that has to grow is replaced by a
+// larger one (at least twice the old size, so the sizes form a geometric
+// series) and the old one is retired, not freed: work already queued, and
+// HIP graphs captured earlier, may still use it.  Retired regions are freed
+// by xpress_release, and their total stays below the live region's size.
 struct Workspace {
     uint64_t* keys = nullptr;
     int64_t rows_cap = 0;
@@ -567,6 +577,9 @@ struct Workspace {
 
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+std::map<int, std::vector<void*>> g_retired;   // per device
+std::map<int, int64_t> g_ws_bytes;             // live + retired bytes per device
+int64_t g_ws_limit = 0;                        // bytes per device; 0 = no limit
 
 int stream_capturing(hipStream_t stream, bool* capturing)
 {
@@ -577,14 +590,19 @@ int stream_capturing(hipStream_t stream, bool* capturing)
     return XPRESS_OK;
 }
 
-// Make sure the (device, stream) workspace holds `rows` atomic slots and a
-// `table` entry table; grows (synchronously) when needed.
-int ensure_workspace(hipStream_t stream, int64_t rows, int64_t table, Workspace** out)
+int64_t grown_cap(int64_t need, int64_t old_cap, int64_t floor_cap)
 {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e);
-    std::lock_guard<std::mutex> lk(g_ws_mu);
+    int64_t cap = need > floor_cap ? need : floor_cap;
+    if (old_cap > 0 && cap < 2 * old_cap) cap = 2 * old_cap;
+    return cap;
+}
+
+// Make sure the (device, stream) workspace holds `rows` atomic slots and a
+// `table` entry table; grows (synchronously) when needed.  Called with
+// g_ws_mu held.
+int ensure_workspace_locked(int dev, hipStream_t stream, int64_t rows, int64_t table,
+                            Workspace** out)
+{
     Workspace& w = g_ws[std::make_pair(dev, stream)];
     const bool grow_rows = rows > w.rows_cap;
     const bool grow_table = table > w.table_cap;
@@ -593,46 +611,54 @@ int ensure_workspace(hipStream_t stream, int64_t rows, int64_t table, Workspace*
         int rc = stream_capturing(stream, &capturing);
         if (rc != XPRESS_OK) return rc;
         if (capturing) return XPRESS_ECAPTURE;
-        // the old buffers may still be in use by queued work on this stream
-        e = hipStreamSynchronize(stream);
-        if (e != hipSuccess) return hip_fail(e);
     }
+    hipError_t e;
     if (grow_rows) {
-        int64_t cap = rows < 4096 ? 4096 : rows;
+        const int64_t cap = grown_cap(rows, w.rows_cap, 4096);
+        if (g_ws_limit > 0 && g_ws_bytes[dev] + cap * 8 > g_ws_limit) return XPRESS_ENOMEM;
         void* p = nullptr;
         e = hipMalloc(&p, (size_t)cap * 8u);
         if (e != hipSuccess) {
             note_hip_error(e);
             return XPRESS_ENOMEM;
         }
+        // zeroed before any kernel can see it (synchronous)
         e = hipMemset(p, 0, (size_t)cap * 8u);
+        if (e == hipSuccess) e = hipDeviceSynchronize();
         if (e != hipSuccess) {
             (void)hipFree(p);
             return hip_fail(e);
         }
-        e = hipDeviceSynchronize();
-        if (e != hipSuccess) {
-            (void)hipFree(p);
-            return hip_fail(e);
-        }
-        if (w.keys) (void)hipFree(w.keys);
+        if (w.keys) g_retired[dev].push_back(w.keys);
         w.keys = static_cast<uint64_t*>(p);
         w.rows_cap = cap;
+        g_ws_bytes[dev] += cap * 8;
     }
     if (grow_table) {
-        int64_t cap = table < 65536 ? 65536 : table;
+        const int64_t cap = grown_cap(table, w.table_cap, 65536);
+        if (g_ws_limit > 0 && g_ws_bytes[dev] + cap * 8 > g_ws_limit) return XPRESS_ENOMEM;
         void* p = nullptr;
         e = hipMalloc(&p, (size_t)cap * 8u);
         if (e != hipSuccess) {
             note_hip_error(e);
             return XPRESS_ENOMEM;
         }
-        if (w.table) (void)hipFree(w.table);
+        if (w.table) g_retired[dev].push_back(w.table);
         w.table = static_cast<uint64_t*>(p);
         w.table_cap = cap;
+        g_ws_bytes[dev] += cap * 8;
     }
     *out = &w;
     return XPRESS_OK;
+}
+
+int ensure_workspace(hipStream_t stream, int64_t rows, int64_t table, Workspace** out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    return ensure_workspace_locked(dev, stream, rows, table, out);
 }
 
 template <int T, bool VEC, int COMBINE>
@@ -722,15 +748,9 @@ int validate(const uint16_t* base, const uint16_t* bias, const int64_t* blk, int
     return XPRESS_OK;
 }
 
-// Plan, workspace and launches shared by both readouts.
-int run_readout(const uint16_t* base, const uint16_t* bias, const int64_t* cand, int64_t* blk,
-                int64_t N, int64_t B, int64_t V, int64_t sb, int64_t sbi, hipStream_t stream)
+RowArgs row_args(const uint16_t* base, const uint16_t* bias, const int64_t* cand, int64_t* blk,
+                 int64_t rows, int64_t B, int64_t V, int64_t sb, int64_t sbi, const Plan& p)
 {
-    int64_t rows = 0;
-    int rc = validate(base, bias, blk, N, B, V, sb, sbi, cand, &rows);
-    if (rc != XPRESS_OK || rows == 0) return rc;
-
-    const Plan p = make_plan(base, bias, rows, V, sb, sbi);
     RowArgs a;
     a.base = base;
     a.bias = bias;
@@ -743,6 +763,31 @@ int run_readout(const uint16_t* base, const uint16_t* bias, const int64_t* cand,
     a.splits = (uint32_t)p.splits;
     a.keys = nullptr;
     a.cand = cand;
+    return a;
+}
+
+// The plan's launches, with a.keys already pointing at its scratch.
+int launch_readout_plan(const RowArgs& a, const Plan& p, hipStream_t stream)
+{
+    hipError_t e = launch_plan(a, p, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    if (p.combine == kTwoPass) {
+        e = launch_reduce_table(a.keys, a.blk, a.cand, a.rows, a.bm1, a.V, a.splits, stream);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return XPRESS_OK;
+}
+
+// Plan, workspace and launches shared by both readouts.
+int run_readout(const uint16_t* base, const uint16_t* bias, const int64_t* cand, int64_t* blk,
+                int64_t N, int64_t B, int64_t V, int64_t sb, int64_t sbi, hipStream_t stream)
+{
+    int64_t rows = 0;
+    int rc = validate(base, bias, blk, N, B, V, sb, sbi, cand, &rows);
+    if (rc != XPRESS_OK || rows == 0) return rc;
+
+    const Plan p = make_plan(base, bias, rows, V, sb, sbi);
+    RowArgs a = row_args(base, bias, cand, blk, rows, B, V, sb, sbi, p);
 
     if (p.combine != kSingle) {
         Workspace* w = nullptr;
@@ -753,13 +798,7 @@ int run_readout(const uint16_t* base, const uint16_t* bias, const int64_t* cand,
         a.keys = words ? w->keys : w->table;
     }
 
-    hipError_t e = launch_plan(a, p, stream);
-    if (e != hipSuccess) return hip_fail(e);
-    if (p.combine == kTwoPass) {
-        e = launch_reduce_table(a.keys, blk, a.cand, a.rows, a.bm1, a.V, a.splits, stream);
-        if (e != hipSuccess) return hip_fail(e);
-    }
-    return XPRESS_OK;
+    return launch_readout_plan(a, p, stream);
 }
 
 }  // namespace
@@ -903,6 +942,28 @@ int xpress_release(void)
             ++it;
         }
     }
+    for (void* p : g_retired[dev]) (void)hipFree(p);
+    g_retired[dev].clear();
+    g_ws_bytes[dev] = 0;
+    return XPRESS_OK;
+}
+
+int xpress_set_workspace_limit(int64_t bytes)
+{
+    if (bytes < 0) return XPRESS_EINVAL;
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    g_ws_limit = bytes;
+    return XPRESS_OK;
+}
+
+int xpress_workspace_bytes(int64_t* live_and_retired)
+{
+    if (!live_and_retired) return XPRESS_EINVAL;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    *live_and_retired = g_ws_bytes[dev];
     return XPRESS_OK;
 }
 

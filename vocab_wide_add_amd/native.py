@@ -74,11 +74,17 @@ def load():
         lib.xpress_reserve.restype = i32
         lib.xpress_release.argtypes = []
         lib.xpress_release.restype = i32
+        lib.xpress_set_workspace_limit.argtypes = [i64]
+        lib.xpress_set_workspace_limit.restype = i32
+        lib.xpress_workspace_bytes.argtypes = [ctypes.POINTER(ctypes.c_int64)]
+        lib.xpress_workspace_bytes.restype = i32
         lib.xpress_set_plan.argtypes = [i32, i32, i32]
         lib.xpress_set_plan.restype = i32
         lib.xpress_describe_plan.argtypes = [vp, vp, i64, i64, i64, i64, i64,
                                              ip, ip, ip, ip, ip]
         lib.xpress_describe_plan.restype = i32
+        lib.xpress_describe_gemm_plan.argtypes = [i64, i64, i64, ip, ip, ip, ip]
+        lib.xpress_describe_gemm_plan.restype = i32
         lib.xpress_bf16_add_round_table.argtypes = [vp, i64, vp, vp]
         lib.xpress_bf16_add_round_table.restype = i32
         lib.xpress_last_hip_error.argtypes = []
@@ -224,6 +230,19 @@ def xpress_release() -> None:
     _check(load().xpress_release(), "xpress_release")
 
 
+def xpress_set_workspace_limit(nbytes: int) -> None:
+    """Cap on the library's workspace per device (0 = none); past it a call
+    returns XPRESS_ENOMEM (raised as XpressError)."""
+    _check(load().xpress_set_workspace_limit(int(nbytes)), "xpress_set_workspace_limit")
+
+
+def xpress_workspace_bytes() -> int:
+    """Bytes of workspace (live and retired) held on the current device."""
+    out = ctypes.c_int64(0)
+    _check(load().xpress_workspace_bytes(ctypes.byref(out)), "xpress_workspace_bytes")
+    return int(out.value)
+
+
 def xpress_set_plan(combine: int = XPRESS_COMBINE_AUTO, splits: int = 0,
                     block_threads: int = 0) -> None:
     _check(load().xpress_set_plan(int(combine), int(splits), int(block_threads)),
@@ -240,6 +259,17 @@ def xpress_describe_plan(base, bias, N: int, B: int, V: int, stride_base_r: int,
     combine, splits, threads, vec, launches = [o.value for o in out]
     return {"combine": COMBINE_NAMES.get(combine, combine), "splits": splits,
             "block_threads": threads, "vector_path": bool(vec), "launches": launches}
+
+
+def xpress_describe_gemm_plan(N: int, B: int, V: int) -> dict:
+    """Launch shape of the readout with in-place bias for (N, B, V): waves
+    per workgroup, vocabulary ranges, workgroups per range and 32-id tiles."""
+    out = [ctypes.c_int(0) for _ in range(4)]
+    _check(load().xpress_describe_gemm_plan(int(N), int(B), int(V),
+                                            *[ctypes.byref(o) for o in out]),
+           "xpress_describe_gemm_plan")
+    waves, ranges, row_wgs, tiles = [o.value for o in out]
+    return {"waves": waves, "ranges": ranges, "row_wgs": row_wgs, "tiles": tiles}
 
 
 def xpress_bf16_add_round_table(a_vals, n_a: int, out, stream=None) -> None:
