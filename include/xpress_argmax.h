@@ -39,6 +39,8 @@ extern "C" {
 #define XPRESS_ECAPTURE 4 /* the workspace would have to grow while the stream
                              is being captured into a graph; call
                              xpress_reserve() before capturing */
+#define XPRESS_ESCRATCH 5 /* the call needs more than the fixed key table of
+                             xpress_add_argmax_to_blk_noalloc */
 
 /*
  * xpress_add_argmax_to_blk -- the fused readout (page and passages above).
@@ -93,6 +95,31 @@ int xpress_add_argmax_to_blk(const uint16_t* base, const uint16_t* bias,
                              int64_t* blk, int64_t N, int64_t B, int64_t V,
                              int64_t stride_base_r, int64_t stride_bias_r,
                              hipStream_t stream);
+
+/*
+ * xpress_add_argmax_to_blk_noalloc -- the same readout as
+ * xpress_add_argmax_to_blk (same arguments, layout rules, result and errors)
+ * for callers that cannot allocate device memory: code being captured into a
+ * HIP graph without a prior xpress_reserve, tight serving loops, harnesses
+ * that forbid allocation.  It never calls hipMalloc, hipFree or any other
+ * allocating routine.  Rows that the plan splits over several workgroups
+ * meet in two passes through a fixed key table of 4096 keys, a device array
+ * built into the library (one copy per GPU, 32 KiB, held until the process
+ * ends); the table holds rows x splits keys, which the automatic plan keeps
+ * below 700, and a call that would need more (e.g. a split count forced with
+ * xpress_set_plan) returns XPRESS_ESCRATCH and queues nothing.  Atomic and
+ * balanced plans set with xpress_set_plan run as two-pass here.  Every call
+ * on one GPU shares that table and overwrites it whole: calls that may run
+ * at the same time on one GPU (e.g. queued on different streams) race and
+ * must not overlap.  Asynchronous, like xpress_add_argmax_to_blk.  The
+ * first call on a device (or xpress_reserve there) looks the table's device
+ * address up with hipGetSymbolAddress; make one of them outside graph
+ * capture before capturing this call.
+ */
+int xpress_add_argmax_to_blk_noalloc(const uint16_t* base, const uint16_t* bias,
+                                     int64_t* blk, int64_t N, int64_t B, int64_t V,
+                                     int64_t stride_base_r, int64_t stride_bias_r,
+                                     hipStream_t stream);
 
 /*
  * xpress_topc_argmax_to_blk -- the top-C readout (XPress kernels page,
@@ -165,7 +192,9 @@ int xpress_readout_gemm_argmax_to_blk(const uint16_t* base, const uint16_t* x,
 /*
  * xpress_reserve -- pre-allocate the workspace the readout would use for
  * (N, B, V) on `stream`'s device and stream, so that a later call -- e.g.
- * one being captured into a HIP graph -- allocates nothing.  Synchronous.
+ * one being captured into a HIP graph -- allocates nothing; it also looks
+ * up the device address of xpress_add_argmax_to_blk_noalloc's table.
+ * Synchronous.
  * Returns XPRESS_OK, XPRESS_EINVAL, XPRESS_ENOMEM or XPRESS_EHIP.
  */
 int xpress_reserve(int64_t N, int64_t B, int64_t V, hipStream_t stream);

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_strings():
     assert native.xpress_version() == "0.1.0"
-    for s in range(5):
+    for s in range(6):
         assert native.xpress_error_string(s) != "unknown status"
     assert native.xpress_error_string(99) == "unknown status"
 

@@ -778,6 +778,32 @@ int launch_readout_plan(const RowArgs& a, const Plan& p, hipStream_t stream)
     return XPRESS_OK;
 }
 
+// The no-allocation variant's key table: a fixed device array, one copy per
+// GPU, shared by every call on that GPU.  Its address on each device is
+// looked up once, with that device current.
+constexpr int64_t kScratchKeys = 4096;
+static __device__ __align__(256) uint64_t scratch[kScratchKeys];
+
+std::mutex g_scratch_mu;
+std::map<int, uint64_t*> g_scratch_ptr;
+
+int scratch_table(uint64_t** out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    auto it = g_scratch_ptr.find(dev);
+    if (it == g_scratch_ptr.end()) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol);
+        it = g_scratch_ptr.emplace(dev, static_cast<uint64_t*>(ptr)).first;
+    }
+    *out = it->second;
+    return XPRESS_OK;
+}
+
 // Plan, workspace and launches shared by both readouts.
 int run_readout(const uint16_t* base, const uint16_t* bias, const int64_t* cand, int64_t* blk,
                 int64_t N, int64_t B, int64_t V, int64_t sb, int64_t sbi, hipStream_t stream)
@@ -876,6 +902,30 @@ int xpress_add_argmax_to_blk(const uint16_t* base, const uint16_t* bias, int64_t
                        stream);
 }
 
+int xpress_add_argmax_to_blk_noalloc(const uint16_t* base, const uint16_t* bias, int64_t* blk,
+                                     int64_t N, int64_t B, int64_t V, int64_t stride_base_r,
+                                     int64_t stride_bias_r, hipStream_t stream)
+{
+    int64_t rows = 0;
+    int rc = validate(base, bias, blk, N, B, V, stride_base_r, stride_bias_r, nullptr, &rows);
+    if (rc != XPRESS_OK || rows == 0) return rc;
+    Plan p = make_plan(base, bias, rows, V, stride_base_r, stride_bias_r);
+    // split rows always meet in two passes here: the table is overwritten
+    // whole by every call, so nothing in the shared array has to start at
+    // zero
+    if (p.combine != kSingle) {
+        p.combine = kTwoPass;
+        p.launches = 2;
+    }
+    RowArgs a = row_args(base, bias, nullptr, blk, rows, B, V, stride_base_r, stride_bias_r, p);
+    if (p.combine == kTwoPass) {
+        if (rows * (int64_t)p.splits > kScratchKeys) return XPRESS_ESCRATCH;
+        rc = scratch_table(&a.keys);
+        if (rc != XPRESS_OK) return rc;
+    }
+    return launch_readout_plan(a, p, stream);
+}
+
 int xpress_topc_argmax_to_blk(const uint16_t* base_c, const uint16_t* bias_c,
                               const int64_t* cand, int64_t* blk, int64_t N, int64_t B,
                               int64_t C, hipStream_t stream)
@@ -922,7 +972,11 @@ int xpress_reserve(int64_t N, int64_t B, int64_t V, hipStream_t stream)
     if (pv.combine == kTwoPass) table = rows * pv.splits;
     if (ps.combine == kTwoPass && rows * ps.splits > table) table = rows * ps.splits;
     Workspace* w = nullptr;
-    return ensure_workspace(stream, rows, table, &w);
+    const int rc = ensure_workspace(stream, rows, table, &w);
+    if (rc != XPRESS_OK) return rc;
+    // also look up the no-allocation variant's table on this device
+    uint64_t* fixed = nullptr;
+    return scratch_table(&fixed);
 }
 
 int xpress_release(void)
@@ -1027,6 +1081,7 @@ const char* xpress_error_string(int status)
         case XPRESS_EHIP: return "a HIP call failed (see xpress_last_hip_error)";
         case XPRESS_ENOMEM: return "could not allocate the device workspace";
         case XPRESS_ECAPTURE: return "the workspace must grow while the stream is capturing; call xpress_reserve first";
+        case XPRESS_ESCRATCH: return "the call needs more than the no-allocation variant's fixed key table (4096 keys)";
         default: return "unknown status";
     }
 }

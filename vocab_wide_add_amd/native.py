@@ -22,6 +22,7 @@ XPRESS_EINVAL = 1
 XPRESS_EHIP = 2
 XPRESS_ENOMEM = 3
 XPRESS_ECAPTURE = 4
+XPRESS_ESCRATCH = 5
 
 XPRESS_COMBINE_AUTO = 0
 XPRESS_COMBINE_SINGLE = 1
@@ -59,6 +60,8 @@ def load():
         ip = ctypes.POINTER(ctypes.c_int)
         lib.xpress_add_argmax_to_blk.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, vp]
         lib.xpress_add_argmax_to_blk.restype = i32
+        lib.xpress_add_argmax_to_blk_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, vp]
+        lib.xpress_add_argmax_to_blk_noalloc.restype = i32
         lib.xpress_topc_argmax_to_blk.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
         lib.xpress_topc_argmax_to_blk.restype = i32
         lib.xpress_readout_gemm_argmax_to_blk.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64,
@@ -154,6 +157,22 @@ def xpress_add_argmax_to_blk(base, bias, blk, N: int, B: int, V: int,
                                         int(V), int(stride_base_r), int(stride_bias_r),
                                         _stream(stream)),
            "xpress_add_argmax_to_blk")
+
+
+def xpress_add_argmax_to_blk_noalloc(base, bias, blk, N: int, B: int, V: int,
+                                     stride_base_r: int, stride_bias_r: int, stream=None) -> None:
+    """The same readout without any device allocation (a fixed key table
+    built into the library, shared by every call on the GPU)."""
+    rows = int(N) * (int(B) - 1)
+    if rows > 0:
+        _span(base, ((rows - 1) * int(stride_base_r) + int(V)) * 2, "base")
+        _span(bias, ((rows - 1) * int(stride_bias_r) + int(V)) * 2, "bias")
+        _span(blk, int(N) * int(B) * 8, "blk")
+    lib = load()
+    _check(lib.xpress_add_argmax_to_blk_noalloc(_ptr(base), _ptr(bias), _ptr(blk), int(N),
+                                                int(B), int(V), int(stride_base_r),
+                                                int(stride_bias_r), _stream(stream)),
+           "xpress_add_argmax_to_blk_noalloc")
 
 
 def xpress_topc_argmax_to_blk(base_c, bias_c, cand, blk, N: int, B: int, C: int,
