@@ -44,8 +44,13 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 LLC_BYTES = 256 * 2 ** 20    # MI355X Infinity Cache
-SRC = os.path.join(ROOT, "vocab_wide_add_amd", "csrc", "xpress_argmax.hip")
-GEMM_SRC = os.path.join(ROOT, "vocab_wide_add_amd", "csrc", "readout_gemm.hip")
+CSRC = os.path.join(ROOT, "vocab_wide_add_amd", "csrc")
+_COMMON = [os.path.join(CSRC, "device_common.h"), os.path.join(CSRC, "host_common.h"),
+           os.path.join(ROOT, "include", "xpress_argmax.h")]
+# every source a kernel's code is compiled from (the readout with in-place
+# bias also runs the key reduction of xpress_argmax.hip)
+SRC = [os.path.join(CSRC, "xpress_argmax.hip")] + _COMMON
+GEMM_SRC = [os.path.join(CSRC, "readout_gemm.hip"), os.path.join(CSRC, "xpress_argmax.hip")] + _COMMON
 
 
 def log(msg):
@@ -53,15 +58,20 @@ def log(msg):
     sys.stderr.flush()
 
 
-def source_digest(src: str = SRC) -> str:
-    """SHA-256 of a kernel source's code: comments removed and whitespace runs
-    collapsed, so that counters recorded for the code stay valid across edits
-    of its comments and are dropped by any change to the code itself."""
-    with open(src, encoding="utf-8") as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", " ", text)
-    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
+def source_digest(src=SRC) -> str:
+    """SHA-256 of the code of every source a kernel is compiled from (a path
+    or a list of paths): comments removed and whitespace runs collapsed, so
+    that counters recorded for the code stay valid across edits of its
+    comments and are dropped by any change to the code itself."""
+    paths = [src] if isinstance(src, str) else list(src)
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode() + b"\0")
+    return h.hexdigest()
 
 
 def traffic_for(workload: str, src: str = SRC):
@@ -77,33 +87,72 @@ def traffic_for(workload: str, src: str = SRC):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(base, bias, w, target_s: float):
-    """The oracle, as is, on the first rows of the workload, rows spread over
-    the host cores.  Returns (result dict, rows checked, oracle answers)."""
-    import oracle
+def cpu_model() -> str:
+    """The host CPU's model string (/proc/cpuinfo), for the baseline's record."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def host_cores() -> int:
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
-    cores = max(1, min(cores, 64))
+    return max(1, min(cores or 1, 64))
+
+
+def cpu_baseline(base, bias, w, target_s: float):
+    """The oracle, as is, on the host cores: three timed runs on all cores
+    (rows spread over threads) and three on one thread, each run as many
+    whole passes over its sample of rows as fit in about target_s / 6
+    seconds; the medians are reported.  Returns (result dict, rows checked,
+    the oracle's answers for those rows)."""
+    import statistics
+    import oracle
+    cores = host_cores()
+    per_run = max(0.2, target_s / 6.0)
     t0 = time.perf_counter()
     oracle.add_argmax_rows(base, bias, 0, 1, w.V, w.stride_base, w.stride_bias)
     t_row = max(time.perf_counter() - t0, 1e-4)
-    rows = int(min(w.rows, max(cores, target_s * cores / t_row)))
-    rows = max(1, rows)
-    # whole passes over the sample until the time budget is spent
-    passes = 0
-    t0 = time.perf_counter()
-    while True:
-        ans = oracle.add_argmax_rows_threaded(base, bias, rows, w.V, w.stride_base,
-                                              w.stride_bias, cores)
-        passes += 1
-        dt = time.perf_counter() - t0
-        if dt >= target_s or passes >= 1000:
-            break
-    gbs = passes * rows * w.V * 4 / dt / 1e9
-    res = {"value": round(gbs, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
-           "rows_per_s": round(passes * rows / dt, 1),
-           "sample": "first %d of %d rows of %s, %d passes, %.1f s on %d threads"
-                     % (rows, w.rows, w.name, passes, dt, cores)}
-    return res, rows, ans
+
+    def runs(rows, threads):
+        rates, ans = [], None
+        for _ in range(3):
+            passes, t0 = 0, time.perf_counter()
+            while True:
+                if threads > 1:
+                    ans = oracle.add_argmax_rows_threaded(base, bias, rows, w.V, w.stride_base,
+                                                          w.stride_bias, threads)
+                else:
+                    ans = oracle.add_argmax_rows(base, bias, 0, rows, w.V, w.stride_base,
+                                                 w.stride_bias)
+                passes += 1
+                dt = time.perf_counter() - t0
+                if dt >= per_run or passes >= 1000:
+                    break
+            rates.append(passes * rows / dt)
+        return rates, ans
+
+    rows_mc = int(min(w.rows, max(cores, per_run * cores / t_row)))
+    rows_st = int(min(w.rows, max(1, per_run / t_row)))
+    mc, ans = runs(rows_mc, cores)
+    st, _ = runs(rows_st, 1)
+    gbs = lambda r: round(r * w.V * 4 / 1e9, 3)
+    res = {"value": gbs(statistics.median(mc)), "unit": "GB/s", "cores": cores, "kind": "oracle",
+           "rows_per_s": round(statistics.median(mc), 1),
+           "runs": [gbs(r) for r in mc],
+           "cpu_model": cpu_model(),
+           "single_thread": {"value": gbs(statistics.median(st)), "unit": "GB/s",
+                             "rows_per_s": round(statistics.median(st), 1),
+                             "runs": [gbs(r) for r in st],
+                             "sample": "first %d rows of %s" % (rows_st, w.name)},
+           "sample": "first %d of %d rows of %s; median of 3 runs of ~%.1f s each on %d threads "
+                     "(and 3 on one thread)" % (rows_mc, w.rows, w.name, per_run, cores)}
+    return res, rows_mc, ans
 
 
 def copy_probe(nbytes: int, reps: int):
@@ -148,6 +197,39 @@ def time_graph(step, steps: int, warmup: int, per_graph: int, reserve):
     return wall, r0.elapsed_time(r1) * 1e-3, reps * per_graph
 
 
+def read_ceiling(native, dev, w, sets: int, stream, reps: int):
+    """The plain two-stream read of the same inputs (xpress_read_probe), one
+    workgroup per row and grid-stride, each timed over `reps` launches with
+    HIP events on the launch stream after 50 untimed ones.  None when the
+    layout is not one the probe reads (equal, 8-element-aligned strides)."""
+    import torch
+    if w.V % 8 or w.stride_base != w.stride_bias or w.stride_base % 8:
+        return None
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = {}
+    for mode, name in ((native.XPRESS_READ_ROWS, "per_row"),
+                       (native.XPRESS_READ_FLAT, "grid_stride")):
+        def probe(k):
+            b, i = dev[k % sets][0], dev[k % sets][1]
+            native.xpress_read_probe(b, i, w.rows, w.V, w.stride_base, mode, sink, stream=stream)
+        for k in range(50):
+            probe(k)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for k in range(reps):
+            probe(k)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        nbytes = w.bytes_read if mode == native.XPRESS_READ_ROWS else \
+            ((w.rows - 1) * w.stride_base + w.V) * 4
+        out[name] = {"us": round(us, 3), "GBps": round(nbytes / us / 1e3, 1), "bytes": nbytes,
+                     "launches": reps}
+    return out
+
+
 def last_set(args, sets: int) -> int:
     """Input set written by the last timed step: step k uses set k % sets; a
     captured graph replays steps 0 .. per_graph - 1."""
@@ -162,12 +244,17 @@ def time_steps(step, steps: int, warmup: int, stream):
     of region 1, GPU seconds of region 1, sorted per-call GPU seconds of
     region 2)."""
     import torch
+    log("warming up: %d steps" % warmup)
+    # the events exist (and have been recorded once) before the timed region,
+    # so that no event creation lands inside it
+    r0 = torch.cuda.Event(enable_timing=True)
+    r1 = torch.cuda.Event(enable_timing=True)
+    r0.record(stream)
+    r1.record(stream)
     for k in range(warmup):
         step(k)
     torch.cuda.synchronize()
     log("timing %d steps" % steps)
-    r0 = torch.cuda.Event(enable_timing=True)
-    r1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     r0.record(stream)
@@ -244,7 +331,16 @@ def bench_readout(args, np, torch, native, workloads):
                                        w.stride_base, w.stride_bias)
     native.xpress_reserve(w.N, w.B, w.V, stream=stream)
 
+    # the binding's checks (tensor spans, stream lookup) once per input set
+    # here; each timed step is then one call of the C entry point, which
+    # validates its arguments itself
+    calls = [native.bind_add_argmax_to_blk(b, i, blk, w.N, w.B, w.V, w.stride_base,
+                                           w.stride_bias, stream=stream) for b, i, blk in dev]
+
     def step(k, st=stream):
+        if st is stream:
+            calls[k % sets]()
+            return
         b, i, blk = dev[k % sets]
         native.xpress_add_argmax_to_blk(b, i, blk, w.N, w.B, w.V, w.stride_base,
                                         w.stride_bias, stream=st)
@@ -264,6 +360,14 @@ def bench_readout(args, np, torch, native, workloads):
     out = result_line("effective HBM GB/s (+ %% of peak) and rows/s, add+argmax N=%d B=%d V=%d"
                       % (w.N, w.B, w.V), name, config, w.bytes_read, w.rows, args.steps,
                       args.warmup, wall, region_gpu, durs, plan["launches"], traffic_for(name))
+    if not args.no_read_ceiling:
+        log("read ceiling")
+        rc = read_ceiling(native, dev, w, sets, stream, max(200, min(args.steps, 1000)))
+        if rc is not None:
+            k_us = out["kernel_us_region_avg"]
+            rc["readout_over_per_row"] = round(rc["per_row"]["us"] / k_us, 4)
+            rc["readout_over_grid_stride"] = round(rc["grid_stride"]["us"] / k_us, 4)
+        out["read_ceiling"] = rc
     if not args.no_cpu_baseline:
         log("cpu baseline")
         cb, nrows, ans = cpu_baseline(base, bias, w, args.cpu_seconds)
@@ -273,6 +377,39 @@ def bench_readout(args, np, torch, native, workloads):
         if not out["checked_equal"]:
             log("MISMATCH against the oracle on the sampled rows")
     return out
+
+
+def bench_read(args, np, torch, native, workloads):
+    """The read ceiling alone as the timed step: xpress_read_probe over the
+    readout's inputs (--read-mode rows: one workgroup per row; flat:
+    grid-stride), for profiling it under the same command shape."""
+    name = args.workload or workloads.BENCH_WORKLOAD
+    w = workloads.WORKLOADS[name]
+    if w.V % 8 or w.stride_base != w.stride_bias or w.stride_base % 8:
+        raise SystemExit("the read probe needs equal, 8-element-aligned strides")
+    log("generating %s" % name)
+    base, bias, blk0 = workloads.generate(w)
+    footprint = base.nbytes + bias.nbytes
+    sets = max(1, math.ceil(2 * LLC_BYTES / footprint) + 1)
+    b_cpu = torch.from_numpy(base.view(np.int16))
+    i_cpu = torch.from_numpy(bias.view(np.int16))
+    dev = [(b_cpu.cuda(), i_cpu.cuda()) for _ in range(sets)]
+    stream = torch.cuda.current_stream()
+    mode = native.XPRESS_READ_ROWS if args.read_mode == "rows" else native.XPRESS_READ_FLAT
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    nbytes = w.bytes_read if mode == native.XPRESS_READ_ROWS else \
+        ((w.rows - 1) * w.stride_base + w.V) * 4
+
+    def step(k, st=stream):
+        b, i = dev[k % sets]
+        native.xpress_read_probe(b, i, w.rows, w.V, w.stride_base, mode, sink, stream=st)
+
+    wall, region_gpu, durs = time_steps(step, args.steps, args.warmup, stream)
+    config = {"workload": name, "op": "read", "mode": args.read_mode, "rows": w.rows, "V": w.V,
+              "bytes_per_step": nbytes, "input_sets": sets, "launch": "stream"}
+    return result_line("plain streaming read of the readout's inputs (%s): effective GB/s"
+                       % args.read_mode, name, config, nbytes, w.rows, args.steps, args.warmup,
+                       wall, region_gpu, durs, 1, None)
 
 
 def bench_topc(args, np, torch, native, workloads):
@@ -574,8 +711,12 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--op", choices=["readout", "topc", "gemm", "latent", "pass"],
+    ap.add_argument("--op", choices=["readout", "topc", "gemm", "latent", "pass", "read"],
                     default="readout")
+    ap.add_argument("--read-mode", choices=["rows", "flat"], default="rows",
+                    help="--op read: one workgroup per row, or grid-stride")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the read-ceiling leg of the readout line")
     ap.add_argument("--graph", type=int, default=0,
                     help="capture this many steps per HIP graph and time graph replays")
     ap.add_argument("--topc-c", type=int, default=1024, choices=[64, 256, 1024, 4096])
@@ -612,6 +753,8 @@ def main():
         out = bench_latent(args, np, torch, native, workloads)
     elif args.op == "pass":
         out = bench_pass(args, np, torch, native, workloads)
+    elif args.op == "read":
+        out = bench_read(args, np, torch, native, workloads)
     else:
         out = bench_readout(args, np, torch, native, workloads)
     print(json.dumps(out))

@@ -373,6 +373,26 @@ int xpress_describe_gemm_plan(int64_t N, int64_t B, int64_t V, int* waves, int* 
 int xpress_bf16_add_round_table(const uint16_t* a_vals, int64_t n_a,
                                 uint16_t* out, hipStream_t stream);
 
+/*
+ * xpress_read_probe -- a plain streaming read of the readout's two inputs,
+ * with no arithmetic on them: the practical read ceiling against which the
+ * readout's rate is reported.  Not part of the readout.  base and bias are
+ * rows rows of V bf16 at row stride `stride` (elements; V and stride
+ * multiples of 8, 16-byte aligned pointers).  mode XPRESS_READ_ROWS reads
+ * every row's V elements with one 256-thread workgroup per row (the
+ * readout's launch shape at a few hundred rows); XPRESS_READ_FLAT sweeps
+ * every element from the first row's start to the last row's end (padding
+ * between rows included) with two workgroups per compute unit in
+ * grid-stride order.  sink is a device pointer to one uint32 that is written
+ * only if the folded data happens to equal a fixed constant (it keeps the
+ * loads live).  Asynchronous.  Returns XPRESS_OK, XPRESS_EINVAL or
+ * XPRESS_EHIP.
+ */
+#define XPRESS_READ_ROWS 0
+#define XPRESS_READ_FLAT 1
+int xpress_read_probe(const uint16_t* base, const uint16_t* bias, int64_t rows, int64_t V,
+                      int64_t stride, int mode, uint32_t* sink, hipStream_t stream);
+
 /* The HIP error code of the last failing HIP call on this thread. */
 int xpress_last_hip_error(void);
 

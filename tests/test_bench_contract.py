@@ -91,3 +91,44 @@ def test_result_line_fields():
     assert out["n_gpus"] == 1 and out["steps"] == 100
     k = out["kernel_us_event_pairs"]
     assert k["min"] <= k["p10"] <= k["p50"] <= k["p90"]
+
+
+def test_digest_covers_every_source_of_the_kernel(tmp_path):
+    """A code change in any file the kernel is built from (a shared header
+    included) invalidates the counter records; comments anywhere do not."""
+    b = _bench()
+    main = tmp_path / "k.hip"
+    main.write_text("int k() { return h(); }\n")
+    h1 = tmp_path / "h.h"
+    h1.write_text("int h() { return 1; }\n")
+    base = b.source_digest([str(main), str(h1)])
+    h1.write_text("// note\nint h() { return 1; }\n")
+    assert b.source_digest([str(main), str(h1)]) == base
+    h1.write_text("int h() { return 2; }\n")
+    assert b.source_digest([str(main), str(h1)]) != base
+    # the readout's and the GEMM readout's lists name their shared sources
+    for name in ("device_common.h", "host_common.h", "xpress_argmax.h", "xpress_argmax.hip"):
+        assert any(p.endswith(name) for p in b.SRC), name
+        assert any(p.endswith(name) for p in b.GEMM_SRC), name
+    assert any(p.endswith("readout_gemm.hip") for p in b.GEMM_SRC)
+
+
+def test_cpu_baseline_legs_on_a_small_workload():
+    """The CPU baseline reports the all-cores median of three runs, the
+    single-thread median of three, the core count and the CPU model, and its
+    answers are the oracle's."""
+    import numpy as np
+    import oracle
+    from vocab_wide_add_amd import workloads
+    b = _bench()
+    w = workloads.WORKLOADS["tiny_n2_b4_v1000"]
+    base, bias, _ = workloads.generate(w)
+    res, rows, ans = b.cpu_baseline(base, bias, w, 0.6)
+    assert res["kind"] == "oracle" and res["unit"] == "GB/s" and res["cores"] >= 1
+    assert len(res["runs"]) == 3 and len(res["single_thread"]["runs"]) == 3
+    assert sorted(res["runs"])[1] == res["value"]
+    assert sorted(res["single_thread"]["runs"])[1] == res["single_thread"]["value"]
+    assert isinstance(res["cpu_model"], str) and res["cpu_model"]
+    assert 1 <= rows <= w.rows
+    want = oracle.add_argmax_rows(base, bias, 0, rows, w.V, w.stride_base, w.stride_bias)
+    assert np.array_equal(ans, want)

@@ -12,7 +12,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRCS = [os.path.join(PKG, "csrc", "xpress_argmax.hip"),
         os.path.join(PKG, "csrc", "readout_gemm.hip"),
-        os.path.join(PKG, "csrc", "latent.hip")]
+        os.path.join(PKG, "csrc", "latent.hip"),
+        os.path.join(PKG, "csrc", "read_probe.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libxpress_argmax.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -90,6 +90,8 @@ def load():
         lib.xpress_describe_gemm_plan.restype = i32
         lib.xpress_bf16_add_round_table.argtypes = [vp, i64, vp, vp]
         lib.xpress_bf16_add_round_table.restype = i32
+        lib.xpress_read_probe.argtypes = [vp, vp, i64, i64, i64, i32, vp, vp]
+        lib.xpress_read_probe.restype = i32
         lib.xpress_last_hip_error.argtypes = []
         lib.xpress_last_hip_error.restype = i32
         lib.xpress_error_string.argtypes = [i32]
@@ -157,6 +159,29 @@ def xpress_add_argmax_to_blk(base, bias, blk, N: int, B: int, V: int,
                                         int(V), int(stride_base_r), int(stride_bias_r),
                                         _stream(stream)),
            "xpress_add_argmax_to_blk")
+
+
+def bind_add_argmax_to_blk(base, bias, blk, N: int, B: int, V: int, stride_base_r: int,
+                           stride_bias_r: int, stream=None):
+    """xpress_add_argmax_to_blk with its arguments marshalled once: checks
+    the tensors' spans and resolves pointers and the stream now, and returns
+    a callable that queues the readout (the library validates the arguments
+    again on every call and the callable raises on a nonzero status).  The
+    tensors must stay alive and in place while the callable is used."""
+    rows = int(N) * (int(B) - 1)
+    if rows > 0:
+        _span(base, ((rows - 1) * int(stride_base_r) + int(V)) * 2, "base")
+        _span(bias, ((rows - 1) * int(stride_bias_r) + int(V)) * 2, "bias")
+        _span(blk, int(N) * int(B) * 8, "blk")
+    fn = load().xpress_add_argmax_to_blk
+    args = (_ptr(base), _ptr(bias), _ptr(blk), int(N), int(B), int(V), int(stride_base_r),
+            int(stride_bias_r), _stream(stream))
+
+    def call():
+        st = fn(*args)
+        if st != XPRESS_OK:
+            raise XpressError(st, "xpress_add_argmax_to_blk")
+    return call
 
 
 def xpress_add_argmax_to_blk_noalloc(base, bias, blk, N: int, B: int, V: int,
@@ -298,6 +323,24 @@ def xpress_bf16_add_round_table(a_vals, n_a: int, out, stream=None) -> None:
     _check(load().xpress_bf16_add_round_table(_ptr(a_vals), int(n_a), _ptr(out),
                                               _stream(stream)),
            "xpress_bf16_add_round_table")
+
+
+XPRESS_READ_ROWS = 0
+XPRESS_READ_FLAT = 1
+
+
+def xpress_read_probe(base, bias, rows: int, V: int, stride: int, mode: int, sink,
+                      stream=None) -> None:
+    """Plain streaming read of base and bias (no arithmetic): the read
+    ceiling the readout is measured against.  mode XPRESS_READ_ROWS (one
+    workgroup per row) or XPRESS_READ_FLAT (grid-stride sweep)."""
+    if int(rows) > 0:
+        _span(base, ((int(rows) - 1) * int(stride) + int(V)) * 2, "base")
+        _span(bias, ((int(rows) - 1) * int(stride) + int(V)) * 2, "bias")
+        _span(sink, 4, "sink")
+    _check(load().xpress_read_probe(_ptr(base), _ptr(bias), int(rows), int(V), int(stride),
+                                    int(mode), _ptr(sink), _stream(stream)),
+           "xpress_read_probe")
 
 
 def xpress_last_hip_error() -> int:
