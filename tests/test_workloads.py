@@ -66,3 +66,25 @@ def test_planted_layout():
     for r in range(12):
         v = (base[r, :77].astype(np.uint32) << 16).view(np.float32)
         assert int(np.argmax(v)) == r % 77 and v.max() == 64.0
+
+
+def test_generated_inputs_match_their_stored_digests():
+    """SHA-256 of every benchmarked input (whole for the small workloads, a
+    prefix of rows for the large ones) against tests/golden/workload_digests.json,
+    written by tests/golden/make_workload_digests.py: a change in the
+    generators, the conversions or the recipes fails here rather than
+    silently changing the inputs."""
+    import importlib.util
+    import json
+    import os
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    spec = importlib.util.spec_from_file_location("make_workload_digests",
+                                                  os.path.join(here, "make_workload_digests.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    with open(os.path.join(here, "workload_digests.json")) as f:
+        stored = json.load(f)
+    now = mod.digests()
+    assert sorted(now) == sorted(stored)
+    for key in stored:
+        assert now[key] == stored[key], key
