@@ -41,7 +41,7 @@ def digests() -> dict:
         out["topc/" + name] = {"base_c": sha(base_c), "bias_c": sha(bias_c), "cand": sha(cand),
                                "blk": sha(blk)}
     for name in ("gemm_tiny_n2_b4_v1000_r64", "gemm_dyadic_n32_b16_v152064_r256",
-                 "gemm_normal_n32_b16_v152064_r256"):
+                 "gemm_normal_n32_b16_v152064_r256", "gemm_negative_n32_b16_v152064_r256"):
         w = workloads.GEMM_WORKLOADS[name]
         lim = None if w.rows <= 64 else PREFIX_ROWS
         base, x, wt, blk = workloads.generate_gemm(w, rows_limit=lim)

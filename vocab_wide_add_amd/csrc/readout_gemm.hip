@@ -106,6 +106,28 @@ __device__ __forceinline__ uint32_t round_pack2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(s, bf16x2));
 }
 
+// Order-preserving map of two packed bf16 patterns: each half, sign and
+// magnitude, becomes the 16-bit two's complement integer +magnitude or
+// -magnitude, so that as signed integers the halves order as the values do,
+// with -0 and +0 both 0 (equal, as the values compare) and a NaN with the
+// sign set below -inf.
+__device__ __forceinline__ uint32_t ord_pair(uint32_t p)
+{
+    typedef short s16x2 __attribute__((ext_vector_type(2)));
+    const s16x2 sign = __builtin_bit_cast(s16x2, p) >> (s16x2){15, 15};  // 0 or -1
+    const s16x2 mag = __builtin_bit_cast(s16x2, p & 0x7FFF7FFFu);
+    return __builtin_bit_cast(uint32_t, (s16x2)((mag ^ sign) - sign));
+}
+
+// Inverse of ord_pair on the high half of a word whose low half is zero:
+// the bf16 pattern of the value in the high half (-0 comes back as +0).
+__device__ __forceinline__ uint32_t unord_hi(uint32_t w)
+{
+    const int32_t o = (int32_t)w >> 16;  // sign-extended 16-bit integer
+    const uint32_t h = o < 0 ? (0x8000u | (uint32_t)(-o)) : (uint32_t)o;
+    return h << 16;
+}
+
 // s_waitcnt vmcnt(n) for a wave-uniform n known only at run time (the
 // instruction takes an immediate): a chain of compares down from N; n above
 // N waits for all.
@@ -168,10 +190,19 @@ __global__ __launch_bounds__(KW * 64) void gemm_readout_kernel(GemmArgs a)
     const uint32_t range = (local / a.row_wgs) * 8u + xcd;
     const uint32_t rw = local % a.row_wgs;
     const uint32_t t0 = (uint32_t)((uint64_t)range * a.tiles / a.ranges);
+    // The first tile as the copies see it.  Before the exact rerun it is
+    // passed through an empty asm statement, so the rerun's copy addresses
+    // are computed afresh instead of being kept in registers (the compiler
+    // would otherwise hold the prologue's 64-bit addresses across the whole
+    // range for it).
+    uint32_t t0c = t0;
     const uint32_t t1 = (uint32_t)((uint64_t)(range + 1u) * a.tiles / a.ranges);
     const int T = (int)(t1 - t0);
     // tiles below Tfull are full; a ragged vocabulary's last tile is not
-    const int Tfull = (T > 0 && t1 * kTileV > a.V) ? T - 1 : T;
+    // (an opaque scalar: the compiler would otherwise keep the comparison
+    // with T as a per-lane flag across the whole range)
+    int Tfull = (T > 0 && t1 * kTileV > a.V) ? T - 1 : T;
+    asm volatile("" : "+s"(Tfull));
 
     // this wave's rows: kGroups groups of 32; the lane's row in group g is
     // g * 32 + l % 32.  The slab a wave takes rotates with the workgroup's
@@ -240,11 +271,11 @@ __global__ __launch_bounds__(KW * 64) void gemm_readout_kernel(GemmArgs a)
     };
     auto issue_base = [&](int j) {
         const int tt = j + AHEAD;
-        if (tt >= 0 && tt < Tfull) dma_base(t0 + (uint32_t)tt, tt % kRing);
+        if (tt >= 0 && tt < Tfull) dma_base(t0c + (uint32_t)tt, tt % kRing);
     };
     auto issue_w = [&](int j) {
         const int tt = j + AHEAD;
-        if (tt >= 0 && tt < T) dma_w(t0 + (uint32_t)tt, tt % kRing);
+        if (tt >= 0 && tt < T) dma_w(t0c + (uint32_t)tt, tt % kRing);
     };
     constexpr int kMaxCount = (AHEAD - 1) * (BLOADS + WPW);
     static_assert(kMaxCount < 64, "wait counts fit vmcnt");
@@ -326,7 +357,7 @@ __global__ __launch_bounds__(KW * 64) void gemm_readout_kernel(GemmArgs a)
     // LDS for a full tile, straight from memory for the ragged last tile
     // (each id at min(id, V - 1); rows past the last read row 0 and never
     // publish).
-    auto load_bv = [&](int g, int i, uint32_t tv, auto full_tag, u32x2 (&bv)[4]) {
+    auto load_bv = [&](int g, int i, uint32_t tv, auto full_tag, u32x2 (&bv)[4]) __attribute__((always_inline)) {
         constexpr bool FULL = decltype(full_tag)::value;
         if constexpr (FULL) {
             const uint32_t lrow = wave * WROWS + 32u * g + (lane & 31u);
@@ -353,6 +384,97 @@ __global__ __launch_bounds__(KW * 64) void gemm_readout_kernel(GemmArgs a)
     const uint32_t arow = lane & 31u;
     const uint32_t aswz = (khalf ^ (arow & (uint32_t)SWZ));
     __syncthreads();
+    // Epilogue modes.  EXACT: compare and select per logit, exact for every
+    // value.  TAGGED: the sum's bf16 bits in the high half of a word and
+    // 31 - (position in the tile) in the low half (positions 8q + jj; the
+    // lane's 4 khalf is in first_id), one signed integer max per logit: the
+    // tile's largest value and, among equal ones, its first position --
+    // exact where the lane's maximum is positive and not NaN.  ORD: the same
+    // after the order-preserving map of the bf16 halves, exact for every
+    // value but NaN.
+    constexpr int kExact = 0, kTaggedRaw = 1, kTaggedOrd = 2;
+    // kTaggedAny: raw or mapped as ord_mode says (one branch per row group
+    // and tile on a workgroup-uniform flag, so both modes share one loop)
+    constexpr int kTaggedAny = 3;
+    bool ord_mode = false;
+    // Running best in the tagged modes: the high half of the (mapped) sum's
+    // word, tag cleared, as an int32; below every candidate at the start.
+    auto reset_best_mode = [&](auto mode_tag) __attribute__((always_inline)) {
+        reset_best();
+        if constexpr (decltype(mode_tag)::value == kTaggedOrd) {
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g) best[g] = __int_as_float(INT32_MIN);
+        }
+    };
+    // The epilogue of row group g on tile i (accumulators in acc[g]).
+    auto epi_group = [&](int g, int i, uint32_t tv, auto full_tag, auto mode_tag) __attribute__((always_inline)) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        constexpr int MODE = decltype(mode_tag)::value;
+        u32x2 bv[4];
+        load_bv(g, i, tv, full_tag, bv);
+        if constexpr (MODE == kExact) {
+            // Within the tile a candidate's id is its position in the tile,
+            // an immediate operand of the select (a wave-uniform id would
+            // have to be copied into a vector register for every candidate:
+            // a select reads at most one scalar operand, and the condition is
+            // one); the running id is held relative to the tile meanwhile
+            // (wrapping arithmetic) and restored after the tile.
+            float tb = best[g];
+            uint32_t tp = bidx[g] - (uint32_t)(kTileV * i);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t s01 =
+                    add_round2(bv[q].x, round_pack2(acc[g][4 * q], acc[g][4 * q + 1]));
+                const uint32_t s23 =
+                    add_round2(bv[q].y, round_pack2(acc[g][4 * q + 2], acc[g][4 * q + 3]));
+                const float sv[4] = {bf16_lo(s01), bf16_hi(s01), bf16_lo(s23), bf16_hi(s23)};
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    // ids past V exist only in a ragged last tile
+                    const bool take =
+                        FULL ? (sv[jj] > tb)
+                             : ((tv + 8u * q + 4u * khalf + jj < a.V) && (sv[jj] > tb));
+                    tb = take ? sv[jj] : tb;
+                    tp = take ? (uint32_t)(8 * q + jj) : tp;
+                }
+            }
+            best[g] = tb;
+            bidx[g] = tp + (uint32_t)(kTileV * i);
+        } else {
+            // The tile's maximum meets the running one with its tag cleared,
+            // so an equal value from a later tile does not replace it.
+            int32_t m = INT32_MIN;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t s01 = add_round2(bv[q].x, round_pack2(acc[g][4 * q], acc[g][4 * q + 1]));
+                uint32_t s23 =
+                    add_round2(bv[q].y, round_pack2(acc[g][4 * q + 2], acc[g][4 * q + 3]));
+                if constexpr (MODE == kTaggedOrd) {
+                    s01 = ord_pair(s01);
+                    s23 = ord_pair(s23);
+                }
+                const int32_t tagged[4] = {
+                    (int32_t)((s01 << 16) | (uint32_t)(31 - 8 * q)),
+                    (int32_t)((s01 & 0xFFFF0000u) | (uint32_t)(30 - 8 * q)),
+                    (int32_t)((s23 << 16) | (uint32_t)(29 - 8 * q)),
+                    (int32_t)((s23 & 0xFFFF0000u) | (uint32_t)(28 - 8 * q))};
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    // ids past V exist only in a ragged last tile
+                    const int32_t c =
+                        FULL ? tagged[jj]
+                             : ((tv + 8u * q + 4u * khalf + jj < a.V) ? tagged[jj] : INT32_MIN);
+                    m = m > c ? m : c;
+                }
+            }
+            const int32_t mv = (int32_t)((uint32_t)m & 0xFFFF0000u);
+            const int32_t tb = __float_as_int(best[g]);
+            const bool take = mv > tb;
+            best[g] = take ? __int_as_float(mv) : best[g];
+            bidx[g] = take ? (uint32_t)(kTileV * i) + (31u - ((uint32_t)m & 0xFFFFu)) : bidx[g];
+        }
+    };
+
     // One tile: copies two tiles ahead; the matrix instructions on w tile i
     // (one A-operand read feeds both row groups); the epilogue (bias rounded
     // to bf16, added to base, rounded, compared); then the wait that lands
@@ -362,18 +484,16 @@ __global__ __launch_bounds__(KW * 64) void gemm_readout_kernel(GemmArgs a)
     // from different waves slow each other down.  Full tiles run in the loop;
     // a ragged last tile runs after it, where x is no longer live, so its
     // clamped loads do not compete with x for registers.
-    auto step = [&](int i, auto full_tag, auto steady_tag, auto ng_tag, auto exact_tag) {
-        constexpr bool FULL = decltype(full_tag)::value;
+    auto step = [&](int i, auto full_tag, auto steady_tag, auto ng_tag, auto mode_tag) __attribute__((always_inline)) {
         constexpr int NG = decltype(ng_tag)::value;  // row groups in use
         // steady: tile i + AHEAD exists and is full, so the copies and the
         // wait count are the fixed ones and the body has no branches
         constexpr bool STEADY = decltype(steady_tag)::value;
-        constexpr bool EXACT = decltype(exact_tag)::value;  // compare-and-select epilogue
         const uint32_t tv = (t0 + (uint32_t)i) * kTileV;
         // base copies now, w copies between the two groups' epilogues: each
         // wave's copies go to the address unit in two smaller bursts
         if constexpr (STEADY) {
-            dma_base(t0 + (uint32_t)(i + AHEAD), (i + AHEAD) % kRing);
+            dma_base(t0c + (uint32_t)(i + AHEAD), (i + AHEAD) % kRing);
         } else {
             issue_base(i);
         }
@@ -415,81 +535,20 @@ __global__ __launch_bounds__(KW * 64) void gemm_readout_kernel(GemmArgs a)
         for (int g = 0; g < kGroups; ++g) {
             if (g == 1) {
                 if constexpr (STEADY) {
-                    dma_w(t0 + (uint32_t)(i + AHEAD), (i + AHEAD) % kRing);
+                    dma_w(t0c + (uint32_t)(i + AHEAD), (i + AHEAD) % kRing);
                 } else {
                     issue_w(i);
                 }
             }
             if (g >= NG) break;
-            u32x2 bv[4];
-            load_bv(g, i, tv, full_tag, bv);
-            if constexpr (EXACT) {
-                // Within the tile a candidate's id is its position in the
-                // tile, an immediate operand of the select (a wave-uniform id
-                // would have to be copied into a vector register for every
-                // candidate: a select reads at most one scalar operand, and
-                // the condition is one); the running id is held relative to
-                // the tile meanwhile (wrapping arithmetic) and restored after
-                // the tile.
-                float tb = best[g];
-                uint32_t tp = bidx[g] - (uint32_t)(kTileV * i);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t s01 =
-                        add_round2(bv[q].x, round_pack2(acc[g][4 * q], acc[g][4 * q + 1]));
-                    const uint32_t s23 =
-                        add_round2(bv[q].y, round_pack2(acc[g][4 * q + 2], acc[g][4 * q + 3]));
-                    const float sv[4] = {bf16_lo(s01), bf16_hi(s01), bf16_lo(s23),
-                                         bf16_hi(s23)};
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        // ids past V exist only in a ragged last tile
-                        const bool take =
-                            FULL ? (sv[jj] > tb)
-                                 : ((tv + 8u * q + 4u * khalf + jj < a.V) && (sv[jj] > tb));
-                        tb = take ? sv[jj] : tb;
-                        tp = take ? (uint32_t)(8 * q + jj) : tp;
-                    }
+            if constexpr (decltype(mode_tag)::value == kTaggedAny) {
+                if (ord_mode) {
+                    epi_group(g, i, tv, full_tag, std::integral_constant<int, kTaggedOrd>{});
+                } else {
+                    epi_group(g, i, tv, full_tag, std::integral_constant<int, kTaggedRaw>{});
                 }
-                best[g] = tb;
-                bidx[g] = tp + (uint32_t)(kTileV * i);
             } else {
-                // Tagged maximum: the sum's bf16 bits in the high half, and
-                // 31 - (position in the tile) in the low half (positions
-                // 8q + jj; the lane's 4 khalf is in first_id).  One signed
-                // integer max per logit keeps the tile's largest value and,
-                // among equal ones, the first position, for positive values;
-                // non-positive maxima are caught after the range.  The tile's
-                // maximum then meets the running one with its tag cleared, so
-                // an equal value from a later tile does not replace it.
-                int32_t m = INT32_MIN;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t s01 =
-                        add_round2(bv[q].x, round_pack2(acc[g][4 * q], acc[g][4 * q + 1]));
-                    const uint32_t s23 =
-                        add_round2(bv[q].y, round_pack2(acc[g][4 * q + 2], acc[g][4 * q + 3]));
-                    const int32_t tagged[4] = {
-                        (int32_t)((s01 << 16) | (uint32_t)(31 - 8 * q)),
-                        (int32_t)((s01 & 0xFFFF0000u) | (uint32_t)(30 - 8 * q)),
-                        (int32_t)((s23 << 16) | (uint32_t)(29 - 8 * q)),
-                        (int32_t)((s23 & 0xFFFF0000u) | (uint32_t)(28 - 8 * q))};
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        // ids past V exist only in a ragged last tile
-                        const int32_t c =
-                            FULL ? tagged[jj]
-                                 : ((tv + 8u * q + 4u * khalf + jj < a.V) ? tagged[jj]
-                                                                          : INT32_MIN);
-                        m = m > c ? m : c;
-                    }
-                }
-                const int32_t mv = (int32_t)((uint32_t)m & 0xFFFF0000u);
-                const int32_t tb = __float_as_int(best[g]);
-                const bool take = mv > tb;
-                best[g] = take ? __int_as_float(mv) : best[g];
-                bidx[g] = take ? (uint32_t)(kTileV * i) + (31u - ((uint32_t)m & 0xFFFFu))
-                               : bidx[g];
+                epi_group(g, i, tv, full_tag, mode_tag);
             }
         }
         // tile i + 1 went out during tile i + 1 - AHEAD; only the copies of
@@ -505,41 +564,97 @@ __global__ __launch_bounds__(KW * 64) void gemm_readout_kernel(GemmArgs a)
         }
         __syncthreads();
     };
-    auto run = [&](auto ng_tag, auto exact_tag) {
-        int i = 0;
+    // Tiles i0 .. T - 1 in one epilogue mode.
+    auto run_from = [&](int i0, auto ng_tag, auto mode_tag) __attribute__((always_inline)) {
+        int i = i0;
         for (; i + AHEAD < Tfull; ++i)
-            step(i, std::true_type{}, std::true_type{}, ng_tag, exact_tag);
-        for (; i < Tfull; ++i) step(i, std::true_type{}, std::false_type{}, ng_tag, exact_tag);
-        if (Tfull < T) step(T - 1, std::false_type{}, std::false_type{}, ng_tag, exact_tag);
+            step(i, std::true_type{}, std::true_type{}, ng_tag, mode_tag);
+        for (; i < Tfull; ++i) step(i, std::true_type{}, std::false_type{}, ng_tag, mode_tag);
+        if (Tfull < T && T - 1 >= i0)
+            step(T - 1, std::false_type{}, std::false_type{}, ng_tag, mode_tag);
     };
-    // both paths pass the same barriers, one per tile.  The tagged epilogue
-    // serves the 2- and 8-wave shapes (measured: 61.0 -> 57.7 us at 480
-    // rows, 29.1 -> 28.6 us at 120 rows); in the one-wave shape, which is
-    // bound by streaming w, the second loop the tagged epilogue needs made
-    // the kernel slower (342 instead of 292 registers, 18.6 -> 29.4 us at 15
-    // rows), so it keeps the compare-and-select epilogue alone.
+    // Tile 0 alone, in whichever of the loop's shapes it has.
+    auto step0 = [&](auto ng_tag, auto mode_tag) __attribute__((always_inline)) {
+        if (AHEAD < Tfull) {
+            step(0, std::true_type{}, std::true_type{}, ng_tag, mode_tag);
+        } else if (0 < Tfull) {
+            step(0, std::true_type{}, std::false_type{}, ng_tag, mode_tag);
+        } else {
+            step(0, std::false_type{}, std::false_type{}, ng_tag, mode_tag);
+        }
+    };
+    // The 2- and 8-wave shapes take a tagged epilogue (measured: 61.0 ->
+    // 57.7 us at 480 rows, 29.1 -> 28.6 us at 120 rows): after tile 0 the
+    // workgroup votes on whether every lane's maximum so far is positive.
+    // If so the raw-bit tags are exact for the whole range (a lane's maximum
+    // only grows); if not -- negative logits, e.g. log-probabilities -- tile
+    // 0's epilogue runs again in the order-preserving mode from the
+    // accumulators and the base tile still in place (no copy of tile 0 + 2
+    // AHEAD has been issued into its buffer yet) and the rest of the range
+    // follows in that mode.  The one-wave shape, which is bound by streaming
+    // w, keeps the compare-and-select epilogue alone (the tagged loops made
+    // it slower: 342 instead of 292 registers, 18.6 -> 29.4 us at 15 rows).
     constexpr bool kTagged = (KW >= 2);
-    if (g1) {
-        run(std::integral_constant<int, 2>{}, std::bool_constant<!kTagged>{});
+    auto run_tagged = [&](auto ng_tag) __attribute__((always_inline)) {
+        if (T <= 0) return;
+        step0(ng_tag, std::integral_constant<int, kTaggedRaw>{});
+        bool nonpos = false;
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+            nonpos |= row_ok[g] && bidx[g] != kNoIndex && __float_as_int(best[g]) <= 0;
+        // (a range of one ragged tile has no later tiles to switch for: the
+        // check after the range covers it)
+        if (__syncthreads_or(nonpos) && 0 < Tfull) {
+            ord_mode = true;
+            reset_best_mode(std::integral_constant<int, kTaggedOrd>{});
+            const uint32_t tv0 = t0 * kTileV;
+#pragma unroll
+            for (int g = 0; g < decltype(ng_tag)::value; ++g)
+                epi_group(g, 0, tv0, std::true_type{}, std::integral_constant<int, kTaggedOrd>{});
+            run_from(1, ng_tag, std::integral_constant<int, kTaggedOrd>{});
+        } else {
+            run_from(1, ng_tag, std::integral_constant<int, kTaggedRaw>{});
+        }
+    };
+    if constexpr (kTagged) {
+        if (g1) {
+            run_tagged(std::integral_constant<int, 2>{});
+        } else {
+            run_tagged(std::integral_constant<int, 1>{});
+        }
     } else {
-        run(std::integral_constant<int, 1>{}, std::bool_constant<!kTagged>{});
+        if (g1) {
+            run_from(0, std::integral_constant<int, 2>{}, std::integral_constant<int, kExact>{});
+        } else {
+            run_from(0, std::integral_constant<int, 1>{}, std::integral_constant<int, kExact>{});
+        }
     }
-    // The tagged maximum is exact where a lane's maximum is positive and not
-    // NaN (bit pattern above +0, at most +inf's).  A positive NaN sum has the
-    // largest bit pattern of all and would win, where the compare-and-select
-    // epilogue never takes a NaN.  Otherwise the whole workgroup covers its range once
-    // more with the exact epilogue: the copies of tiles 0 .. AHEAD - 1 go out
-    // again in the loop's order (x is still in registers) and every wave
-    // passes the same barriers.  Every copy of the first run has landed and
-    // been read before its last barrier.
+    // Back to plain bf16 bit patterns in the high half (the low half is zero).
+    if (ord_mode) {
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) best[g] = __uint_as_float(unord_hi(__float_as_uint(best[g])));
+    }
+    // The tagged maxima are exact except where a lane's maximum is not
+    // positive in the raw mode, or is NaN (a NaN sum has a larger pattern than
+    // +inf in either mode, where the compare-and-select epilogue never takes a
+    // NaN).  Otherwise the whole workgroup covers its
+    // range once more with the exact epilogue: the copies of tiles
+    // 0 .. AHEAD - 1 go out again in the loop's order (x is still in
+    // registers) and every wave passes the same barriers.  Every copy of the
+    // first run has landed and been read before its last barrier.
     if constexpr (kTagged) {
         bool redo = false;
 #pragma unroll
-        for (int g = 0; g < kGroups; ++g)
-            redo |= row_ok[g] && bidx[g] != kNoIndex &&
-                    (__float_as_int(best[g]) <= 0 || __float_as_int(best[g]) > 0x7F800000);
+        for (int g = 0; g < kGroups; ++g) {
+            const uint32_t mag = __float_as_uint(best[g]) & 0x7FFFFFFFu;
+            const bool bad = ord_mode ? (mag > 0x7F800000u)
+                                      : (__float_as_int(best[g]) <= 0 ||
+                                         __float_as_int(best[g]) > 0x7F800000);
+            redo |= row_ok[g] && bidx[g] != kNoIndex && bad;
+        }
         if (__syncthreads_or(redo)) {
             reset_best();
+            asm volatile("" : "+s"(t0c));
             issue_w(-AHEAD);
             issue_base(-AHEAD);
             int later2 = 0;
@@ -549,10 +664,13 @@ __global__ __launch_bounds__(KW * 64) void gemm_readout_kernel(GemmArgs a)
             }
             wait_vmcnt_dyn<kMaxCount>(later2);
             __syncthreads();
-            if (g1) {
-                run(std::integral_constant<int, 2>{}, std::true_type{});
+            // recomputed rather than held across the range
+            uint32_t w0 = wrow0;
+            asm volatile("" : "+s"(w0));
+            if (w0 + 32u < a.rows) {
+                run_from(0, std::integral_constant<int, 2>{}, std::integral_constant<int, kExact>{});
             } else {
-                run(std::integral_constant<int, 1>{}, std::true_type{});
+                run_from(0, std::integral_constant<int, 1>{}, std::integral_constant<int, kExact>{});
             }
         }
     }

@@ -262,6 +262,7 @@ class GemmWorkload:
     R: int
     seed: int
     dyadic: bool  # x, w on the grid k/8, |k| <= 8: every fp32 partial sum is exact
+    base_mean: float = 0.0  # mean of base; negative for log-probability-like logits
 
     @property
     def rows(self) -> int:
@@ -286,6 +287,9 @@ GEMM_WORKLOADS = {
         GemmWorkload("gemm_dyadic_n32_b16_v152064_r256", 32, 16, 152064, 256, 22, True),
         GemmWorkload("gemm_normal_n32_b16_v152064_r256", 32, 16, 152064, 256, 23, False),
         GemmWorkload("gemm_normal_n1_b16_v152064_r256", 1, 16, 152064, 256, 24, False),
+        # every logit negative (base ~ N(-20, 4^2)): log-probability-like rows
+        GemmWorkload("gemm_negative_n32_b16_v152064_r256", 32, 16, 152064, 256, 25, False,
+                     base_mean=-20.0),
     ]
 }
 
@@ -296,7 +300,7 @@ def generate_gemm(w: GemmWorkload, rows_limit: Optional[int] = None):
     """Inputs of the readout with in-place bias.
 
     Recipe (``SeedSequence(seed).spawn(4)``: base, x, w and id streams):
-    base ~ N(0, 4^2) in float32 rounded to bf16, [rows, V]; for the dyadic
+    base ~ N(base_mean, 4^2) in float32 rounded to bf16, [rows, V]; for the dyadic
     workloads x and w are integers uniform on [-8, 8] divided by 8 (exact in
     bf16; every product is a multiple of 1/64 of magnitude <= 1, so any fp32
     partial sum over R <= 4096 terms is exact and the bias is order-free);
@@ -309,6 +313,8 @@ def generate_gemm(w: GemmWorkload, rows_limit: Optional[int] = None):
     keep = w.rows if rows_limit is None else min(w.rows, rows_limit)
     gb = np.random.Generator(np.random.PCG64(s_base))
     base = gb.standard_normal((keep, w.V), dtype=np.float32) * np.float32(4.0)
+    if w.base_mean:
+        base = base + np.float32(w.base_mean)
     gx = np.random.Generator(np.random.PCG64(s_x))
     gw = np.random.Generator(np.random.PCG64(s_w))
     if w.dyadic:
