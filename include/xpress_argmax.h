@@ -340,6 +340,20 @@ int xpress_workspace_bytes(int64_t* live_and_retired);
 int xpress_set_plan(int combine, int splits, int block_threads);
 
 /*
+ * xpress_set_reverse_order -- a debug setting for checking that results do
+ * not depend on the order in which workgroups run.  With reversed nonzero,
+ * later launches of the streaming readout (every combine, and the top-C
+ * readout when it takes that path) visit their (row, split) units, or their
+ * balanced ranges, from last to first, and the readout with in-place bias
+ * maps its workgroups to (vocabulary range, row block) pairs from last to
+ * first within each XCD; the work each workgroup does is unchanged, only
+ * which runs early and which late, so the combines see their keys arrive in
+ * another order.  Every result must be bit-identical to the default order's.
+ * Process-wide; 0 restores the default.  Always returns XPRESS_OK.
+ */
+int xpress_set_reverse_order(int reversed);
+
+/*
  * xpress_describe_plan -- what a call with these sizes and alignments would
  * launch: *combine, *splits, *block_threads, *vector_path (1 = 16-byte loads)
  * and *launches.  Pure host computation.  Returns XPRESS_OK or XPRESS_EINVAL.

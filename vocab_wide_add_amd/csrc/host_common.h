@@ -22,6 +22,10 @@ XPRESS_INTERNAL int device_cus();
 
 XPRESS_INTERNAL bool is_aligned16(const void* p);
 
+// Whether launches should visit their work units in reverse order (the
+// debug setting of xpress_set_reverse_order).
+XPRESS_INTERNAL bool reverse_order();
+
 XPRESS_INTERNAL bool ranges_overlap(const void* p0, size_t n0, const void* p1, size_t n1);
 
 // The (device, stream) workspace's key table, grown to at least `entries`

@@ -85,6 +85,7 @@ struct GemmArgs {
     uint32_t tiles;        // ceil(V / kTileV)
     uint32_t ranges;       // vocabulary ranges (a multiple of 8)
     uint32_t row_wgs;      // workgroups per range
+    uint32_t reverse;      // nonzero: workgroups mapped last to first
 };
 
 // The row of a 32-row group whose B operand (x) or A operand (w) lane l
@@ -184,7 +185,9 @@ __global__ __launch_bounds__(KW * 64) void gemm_readout_kernel(GemmArgs a)
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t khalf = lane >> 5;
-    const uint32_t b = blockIdx.x;
+    // (reversed, the grid's last workgroup takes the first pair; the grid is
+    // a multiple of 8, so a range's workgroups still share an XCD)
+    const uint32_t b = a.reverse ? gridDim.x - 1u - blockIdx.x : blockIdx.x;
     const uint32_t xcd = b & 7u;
     const uint32_t local = b >> 3;
     const uint32_t range = (local / a.row_wgs) * 8u + xcd;
@@ -791,6 +794,7 @@ extern "C" int xpress_readout_gemm_argmax_to_blk(const uint16_t* base, const uin
     a.tiles = p.tiles;
     a.row_wgs = p.row_wgs;
     a.ranges = p.ranges;
+    a.reverse = reverse_order() ? 1u : 0u;
 
     int rc = workspace_table(stream, rows * (int64_t)p.ranges, &a.table);
     if (rc != XPRESS_OK) return rc;

@@ -38,6 +38,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -161,6 +162,7 @@ struct RowArgs {
     uint64_t* keys;       // ATOMIC: [rows] key-and-count words;
                           // TWO_PASS: [rows, splits] key table
     const int64_t* cand;  // top-C readout: [rows, V] candidate ids, else null
+    uint32_t reverse;     // nonzero: units (ranges) visited last to first
 };
 
 enum Combine { kSingle = XPRESS_COMBINE_SINGLE, kAtomic = XPRESS_COMBINE_ATOMIC,
@@ -208,7 +210,8 @@ template <int T, int UNROLL, bool VEC, int COMBINE>
 __global__ __launch_bounds__(T) void readout_kernel(RowArgs a)
 {
     const uint32_t units = a.rows * a.splits;
-    for (uint32_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    for (uint32_t k = blockIdx.x; k < units; k += gridDim.x) {
+        const uint32_t unit = a.reverse ? units - 1u - k : k;
         const uint32_t row = unit / a.splits;
         const uint32_t split = unit - row * a.splits;
         const uint16_t* rb = a.base + (int64_t)row * a.stride_base;
@@ -269,8 +272,9 @@ __global__ __launch_bounds__(T) void readout_balanced_kernel(RowArgs a)
     const uint64_t nvec = a.V / 8u;
     const uint64_t q = (uint64_t)a.rows * nvec;
     const uint64_t g = gridDim.x;
-    const uint64_t x1 = ((uint64_t)blockIdx.x + 1u) * q / g;
-    uint64_t x = (uint64_t)blockIdx.x * q / g;
+    const uint64_t bid = a.reverse ? g - 1u - blockIdx.x : blockIdx.x;
+    const uint64_t x1 = (bid + 1u) * q / g;
+    uint64_t x = bid * q / g;
     while (x < x1) {
         const uint32_t row = (uint32_t)(x / nvec);
         const uint64_t row0 = (uint64_t)row * nvec;
@@ -453,9 +457,11 @@ struct Plan {
     bool vec;
     int launches;
     uint32_t grid;  // kBalanced: total workgroups
+    bool reverse;   // units visited last to first (debug)
 };
 
 std::mutex g_plan_mu;
+std::atomic<int> g_reverse_order{0};
 int g_override_combine = XPRESS_COMBINE_AUTO;
 int g_override_splits = 0;
 int g_override_threads = 0;
@@ -557,6 +563,7 @@ Plan make_plan(const uint16_t* base, const uint16_t* bias, int64_t rows, int64_t
     p.combine = combine;
     p.splits = (int)s;
     p.launches = (p.combine == kTwoPass) ? 2 : 1;
+    p.reverse = reverse_order();
     return p;
 }
 
@@ -763,6 +770,7 @@ RowArgs row_args(const uint16_t* base, const uint16_t* bias, const int64_t* cand
     a.splits = (uint32_t)p.splits;
     a.keys = nullptr;
     a.cand = cand;
+    a.reverse = p.reverse ? 1u : 0u;
     return a;
 }
 
@@ -857,6 +865,8 @@ int device_cus()
 }
 
 bool is_aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool reverse_order() { return g_reverse_order.load() != 0; }
 
 bool ranges_overlap(const void* p0, size_t n0, const void* p1, size_t n1)
 {
@@ -1033,6 +1043,12 @@ int xpress_set_plan(int combine, int splits, int block_threads)
     g_override_combine = combine;
     g_override_splits = splits;
     g_override_threads = block_threads;
+    return XPRESS_OK;
+}
+
+int xpress_set_reverse_order(int reversed)
+{
+    g_reverse_order.store(reversed ? 1 : 0);
     return XPRESS_OK;
 }
 

@@ -83,6 +83,8 @@ def load():
         lib.xpress_workspace_bytes.restype = i32
         lib.xpress_set_plan.argtypes = [i32, i32, i32]
         lib.xpress_set_plan.restype = i32
+        lib.xpress_set_reverse_order.argtypes = [i32]
+        lib.xpress_set_reverse_order.restype = i32
         lib.xpress_describe_plan.argtypes = [vp, vp, i64, i64, i64, i64, i64,
                                              ip, ip, ip, ip, ip]
         lib.xpress_describe_plan.restype = i32
@@ -291,6 +293,11 @@ def xpress_set_plan(combine: int = XPRESS_COMBINE_AUTO, splits: int = 0,
                     block_threads: int = 0) -> None:
     _check(load().xpress_set_plan(int(combine), int(splits), int(block_threads)),
            "xpress_set_plan")
+
+
+def xpress_set_reverse_order(reversed_: bool) -> None:
+    """Debug: later launches visit their work units from last to first."""
+    _check(load().xpress_set_reverse_order(1 if reversed_ else 0), "xpress_set_reverse_order")
 
 
 def xpress_describe_plan(base, bias, N: int, B: int, V: int, stride_base_r: int,
