@@ -125,7 +125,8 @@ def test_order_map_orders_every_pattern_as_its_value():
     and one with the sign set below -inf, and the inverse gives back the
     pattern (+0 for -0)."""
     pats = np.arange(65536, dtype=np.uint32)
-    vals = _f32(pats).astype(np.float64)
+    with np.errstate(invalid="ignore"):      # NaN patterns widen to NaN
+        vals = _f32(pats).astype(np.float64)
     mapped = np.array([_ord16(p) for p in pats], np.uint16).view(np.int16).astype(np.int64)
     fin = ~np.isnan(vals)
     order = np.argsort(vals[fin], kind="stable")
