@@ -678,9 +678,10 @@ __global__ void __launch_bounds__(kThreads) latent_mix_staged(MixArgs a)
 
     // Every load here goes out at once, older than the chunk loads the
     // contraction counts: the token ids (they gate the embedding copies),
-    // the mixer slice and the cache rows.  The slice is stored to LDS before
-    // any chunk copy is issued, so the wait for it covers these loads only
-    // (a load-then-store loop would pay one memory latency per pass).
+    // the mixer slice and the cache rows.  Only the token ids are waited for
+    // before the chunk copies go out; the slice is stored to LDS after the
+    // contraction (its loads, older than the copies, have landed by the
+    // first chunk's wait), so the copies do not wait for it.
     constexpr int kN = DmaRows<kSlabRows>::kN;
     int64_t tok[kN];
 #pragma unroll
@@ -691,6 +692,9 @@ __global__ void __launch_bounds__(kThreads) latent_mix_staged(MixArgs a)
         const int64_t* tp = (slot == 0) ? a.am1 + n : a.blk + (size_t)n * B + slot - 1;
         tok[j] = *tp;
     }
+    // the token loads stay ahead of the loads below (waiting for them then
+    // leaves the slice and cache loads in flight)
+    asm volatile("" ::: "memory");
     constexpr int kMixPer = kMaxB * kMaxB * 4 / kThreads;
     static_assert(kMixPer * kThreads == kMaxB * kMaxB * 4, "mixer slice split over threads");
     const uint32_t mix_chunks = B * B * 4;
@@ -721,11 +725,6 @@ __global__ void __launch_bounds__(kThreads) latent_mix_staged(MixArgs a)
         // beyond the tile's blocks are never read back)
         if (i < rows && !ok) zero_row |= 1u << j;
     }
-#pragma unroll
-    for (int q = 0; q < kMixPer; ++q) {
-        const uint32_t c = tid + q * kThreads;
-        if (c < mix_chunks) mixs_dyn[c] = mreg[q];
-    }
     const uint16_t* bbase[1] = {a.wlat + (size_t)(c0 + 8 * wave + (lane >> 3)) * R};
     DmaRows<kSlabRows> da;
     DmaRows<kTile> db;
@@ -733,6 +732,12 @@ __global__ void __launch_bounds__(kThreads) latent_mix_staged(MixArgs a)
     dma_setup(db, bbase, lane, wave);
     f32x16 acc[1] = {};
     staged_mma<kSlabRows, kTile, 1>(acc, da, db, lds_a, lds_b, (int)(R / kKC), tid, zero_row);
+    // the mixer slice, read by the mixer after the barrier below
+#pragma unroll
+    for (int q = 0; q < kMixPer; ++q) {
+        const uint32_t c = tid + q * kThreads;
+        if (c < mix_chunks) mixs_dyn[c] = mreg[q];
+    }
     // x = cache + projection, into LDS over the A staging area (free after
     // the contraction's last barrier)
     static_assert(kSlabRows * kPad * sizeof(float) <= sizeof(lds_a), "x tile fits the ring");
