@@ -335,6 +335,29 @@ __device__ __forceinline__ float swiglu(float g, float v)
     return g * __builtin_amdgcn_rcpf(1.0f + expf(-g)) * v;
 }
 
+// bf16(swiglu) of a wave's 16 accumulator values, stored to m for the rows
+// that exist.  All sixteen are formed first, outside any branch, so that
+// their exponentials interleave; only a slab that reaches past the last row
+// takes the per-element check.  row0: the slab's first row.
+__device__ __forceinline__ void store_m_tile(uint16_t* m, uint32_t ldm, uint32_t col,
+                                             const f32x16& g, const f32x16& v, uint32_t row0,
+                                             uint32_t rows, int lane)
+{
+    uint16_t mv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mv[r] = to_bf16(swiglu(g[r], v[r]));
+    if (row0 + kTile <= rows) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m[(size_t)(row0 + acc_row(r, lane)) * ldm + col] = mv[r];
+    } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const uint32_t rr = row0 + acc_row(r, lane);
+            if (rr < rows) m[(size_t)rr * ldm + col] = mv[r];
+        }
+    }
+}
+
 // One workgroup per (32 * WR rows, 32 hidden units); g and v share A.
 template <int WR, int WK>
 __global__ void __launch_bounds__(kThreads) latent_gate_kernel(GateArgs a)
@@ -357,19 +380,19 @@ __global__ void __launch_bounds__(kThreads) latent_gate_kernel(GateArgs a)
     f32x16 acc[2] = {};
     mma_k<2>(acc, ap, bp, wk * steps * 16, steps, ~0u);
     if constexpr (WK == 1) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const uint32_t rr = i0 + wr * kTile + acc_row(r, lane);
-            if (rr < a.rows) a.m[(size_t)rr * a.H + h0 + (lane & 31)] = to_bf16(swiglu(acc[0][r], acc[1][r]));
-        }
+        store_m_tile(a.m, a.H, h0 + (lane & 31), acc[0], acc[1], i0 + wr * kTile, a.rows, lane);
     } else {
         store_tile(&part[0][wk][wr * kTile * kPad], acc[0], lane);
         store_tile(&part[1][wk][wr * kTile * kPad], acc[1], lane);
         __syncthreads();
-        for (int e = tid; e < kRows * kTile; e += kThreads) {
-            const int r = e >> 5, c = e & 31;
-            if (i0 + r >= a.rows) continue;
-            const int o = r * kPad + c;
+        // every element's value first, outside any branch (their
+        // exponentials interleave), then the stores for the rows that exist
+        constexpr int kPer = kRows * kTile / kThreads;
+        uint16_t mv[kPer];
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const int e = tid + q * kThreads;
+            const int o = (e >> 5) * kPad + (e & 31);
             float gs, vs;
             if constexpr (WK == 4) {
                 gs = (part[0][0][o] + part[0][1][o]) + (part[0][2][o] + part[0][3][o]);
@@ -378,7 +401,13 @@ __global__ void __launch_bounds__(kThreads) latent_gate_kernel(GateArgs a)
                 gs = part[0][0][o] + part[0][1][o];
                 vs = part[1][0][o] + part[1][1][o];
             }
-            a.m[(size_t)(i0 + r) * a.H + h0 + c] = to_bf16(swiglu(gs, vs));
+            mv[q] = to_bf16(swiglu(gs, vs));
+        }
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const int e = tid + q * kThreads;
+            const int r = e >> 5, c = e & 31;
+            if (i0 + r < a.rows) a.m[(size_t)(i0 + r) * a.H + h0 + c] = mv[q];
         }
     }
 }
@@ -609,14 +638,8 @@ __global__ void __launch_bounds__(kThreads) latent_gate_staged(GateArgs a)
     staged_mma<kSlabRows, kB, 2 * NH>(acc, da, db, lds_a, lds_b, (int)(a.R / kKC), tid, 0u);
 #pragma unroll
     for (int t = 0; t < NH; ++t) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const uint32_t rr = i0 + kTile * wave + acc_row(r, lane);
-            if (rr < a.rows) {
-                a.m[(size_t)rr * a.H + h0 + kTile * t + (lane & 31)] =
-                    to_bf16(swiglu(acc[t][r], acc[NH + t][r]));
-            }
-        }
+        store_m_tile(a.m, a.H, h0 + kTile * t + (lane & 31), acc[t], acc[NH + t],
+                     i0 + kTile * wave, a.rows, lane);
     }
 }
 
