@@ -396,9 +396,6 @@ __global__ __launch_bounds__(KW * 64) void gemm_readout_kernel(GemmArgs a)
     // after the order-preserving map of the bf16 halves, exact for every
     // value but NaN.
     constexpr int kExact = 0, kTaggedRaw = 1, kTaggedOrd = 2;
-    // kTaggedAny: raw or mapped as ord_mode says (one branch per row group
-    // and tile on a workgroup-uniform flag, so both modes share one loop)
-    constexpr int kTaggedAny = 3;
     bool ord_mode = false;
     // Running best in the tagged modes: the high half of the (mapped) sum's
     // word, tag cleared, as an int32; below every candidate at the start.
@@ -544,15 +541,7 @@ __global__ __launch_bounds__(KW * 64) void gemm_readout_kernel(GemmArgs a)
                 }
             }
             if (g >= NG) break;
-            if constexpr (decltype(mode_tag)::value == kTaggedAny) {
-                if (ord_mode) {
-                    epi_group(g, i, tv, full_tag, std::integral_constant<int, kTaggedOrd>{});
-                } else {
-                    epi_group(g, i, tv, full_tag, std::integral_constant<int, kTaggedRaw>{});
-                }
-            } else {
-                epi_group(g, i, tv, full_tag, mode_tag);
-            }
+            epi_group(g, i, tv, full_tag, mode_tag);
         }
         // tile i + 1 went out during tile i + 1 - AHEAD; only the copies of
         // the tiles after that may remain
