@@ -87,6 +87,13 @@ __device__ __forceinline__ uint16_t to_bf16(float x)
 
 __device__ __forceinline__ float from_bf16(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
+// bf16 element e (0 .. 7) of eight packed in a 16-byte vector, widened
+__device__ __forceinline__ float bf16_at(const u32x4& v, int e)
+{
+    const uint32_t w = (e < 2) ? v.x : (e < 4) ? v.y : (e < 6) ? v.z : v.w;
+    return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+}
+
 // Workgroup b's (row tile, column tile).  With xmap the column tiles of one
 // row tile share an XCD (workgroup b runs on XCD b % 8), so the activation
 // rows they all read are fetched into that XCD's L2 once; otherwise the row
@@ -232,6 +239,50 @@ __device__ __forceinline__ void mix_tile(const float* xs, const uint16_t* mixs, 
         mix_chains<8>(xs, mixs, nb, B, n0, c0, R, u_out, ub_out, tid);
     } else {
         mix_chains<1>(xs, mixs, nb, B, n0, c0, R, u_out, ub_out, tid);
+    }
+}
+
+// The folded mixer for tiles of many blocks (the staged kernel, B <= 16),
+// from a transposed fp32 copy of the mixer slice: mixt[((b - 1) * 32 + c) *
+// kMixT + j] = mixl[b, j, c0 + c], zero for j >= B.  A thread takes one
+// (block, channel): the block's x values for that channel go into
+// registers once, and each slot's sixteen weights come in four 16-byte LDS
+// reads (the rows are padded to 20 floats so that sixteen consecutive
+// channels' reads fall on different banks).  The sums are formed in the
+// same order as mix_chains (j ascending from +0; the padded j add exactly
+// zero), so the two give the same bits.
+constexpr uint32_t kMixT = 20;
+
+__device__ __forceinline__ void mix_tile_t(const float* xs, const float* mixt, uint32_t nb,
+                                           uint32_t B, uint32_t n0, uint32_t c0, uint32_t R,
+                                           float* u_out, uint16_t* ub_out, int tid)
+{
+    const uint32_t bm1 = B - 1;
+    for (uint32_t t = tid; t < nb * kTile; t += kThreads) {
+        const uint32_t lb = t >> 5, c = t & 31;
+        float x[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) x[j] = (uint32_t)j < B ? xs[(lb * B + j) * kPad + c] : 0.0f;
+        float* urow = u_out + ((size_t)(n0 + lb) * bm1) * R + c0 + c;
+        uint16_t* ubrow = ub_out + ((size_t)(n0 + lb) * bm1) * R + c0 + c;
+#pragma unroll 3
+        for (uint32_t b = 1; b < B; ++b) {
+            const float* mr = mixt + ((b - 1) * kTile + c) * kMixT;
+            float m[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 v = *reinterpret_cast<const float4*>(mr + 4 * q);
+                m[4 * q] = v.x;
+                m[4 * q + 1] = v.y;
+                m[4 * q + 2] = v.z;
+                m[4 * q + 3] = v.w;
+            }
+            float acc = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc = fmaf(m[j], x[j], acc);
+            urow[(size_t)(b - 1) * R] = acc;
+            ubrow[(size_t)(b - 1) * R] = to_bf16(acc);
+        }
     }
 }
 
@@ -755,11 +806,33 @@ __global__ void __launch_bounds__(kThreads) latent_mix_staged(MixArgs a)
     dma_setup(db, bbase, lane, wave);
     f32x16 acc[1] = {};
     staged_mma<kSlabRows, kTile, 1>(acc, da, db, lds_a, lds_b, (int)(R / kKC), tid, zero_row);
-    // the mixer slice, read by the mixer after the barrier below
+    // the mixer slice, read by the mixer after the barrier below: for B <= 16
+    // transposed to fp32 (mix_tile_t), else as loaded (mix_tile)
+    const bool transposed = B <= 16;
+    float* mixt = reinterpret_cast<float*>(mixs_dyn);
+    if (transposed) {
 #pragma unroll
-    for (int q = 0; q < kMixPer; ++q) {
-        const uint32_t c = tid + q * kThreads;
-        if (c < mix_chunks) mixs_dyn[c] = mreg[q];
+        for (int q = 0; q < kMixPer; ++q) {
+            const uint32_t c = tid + q * kThreads;
+            if (c < mix_chunks) {
+                const uint32_t bj = c >> 2, b = bj / B, j = bj - b * B, c8 = (c & 3) * 8;
+                if (b >= 1) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        mixt[((b - 1) * kTile + c8 + e) * kMixT + j] = bf16_at(mreg[q], e);
+                    }
+                }
+            }
+        }
+        for (uint32_t i = tid; i < (B - 1) * kTile; i += kThreads) {
+            for (uint32_t j = B; j < 16; ++j) mixt[i * kMixT + j] = 0.0f;
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < kMixPer; ++q) {
+            const uint32_t c = tid + q * kThreads;
+            if (c < mix_chunks) mixs_dyn[c] = mreg[q];
+        }
     }
     // x = cache + projection, into LDS over the A staging area (free after
     // the contraction's last barrier)
@@ -770,7 +843,11 @@ __global__ void __launch_bounds__(kThreads) latent_mix_staged(MixArgs a)
         xs[(kTile * wave + acc_row(r, lane)) * kPad + (lane & 31)] = acc[0][r] + xh[r];
     }
     __syncthreads();
-    mix_tile(xs, mixs, nb, B, n0, c0, R, a.u, a.ub, tid);
+    if (transposed) {
+        mix_tile_t(xs, mixt, nb, B, n0, c0, R, a.u, a.ub, tid);
+    } else {
+        mix_tile(xs, mixs, nb, B, n0, c0, R, a.u, a.ub, tid);
+    }
 }
 
 // Workgroup shape per kernel: 1, 2 or 4 row slabs of the direct kernels, 8
@@ -943,7 +1020,9 @@ int xpress_latent_pass(const int64_t* blk, const int64_t* am1, const uint16_t* x
         return XPRESS_EINVAL;
     }
 
-    const size_t mix_lds = (size_t)B * B * kTile * 2u;
+    // the staged kernel keeps a transposed fp32 copy of the slice for B <= 16
+    const size_t mix_lds = (wr_mix == kStaged && B <= 16) ? (size_t)(B - 1) * kTile * kMixT * 4u
+                                                          : (size_t)B * B * kTile * 2u;
     const void* mix_fn = wr_mix == kStaged ? reinterpret_cast<const void*>(&latent_mix_staged)
                        : wr_mix == 4 ? reinterpret_cast<const void*>(&latent_mix_kernel<4, 1>)
                        : wr_mix == 2 ? reinterpret_cast<const void*>(&latent_mix_kernel<2, 2>)
