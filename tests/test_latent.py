@@ -116,6 +116,41 @@ def test_latent_large_with_forced_tiles(tiles):
     assert_parity(got, want, d, inter, w.B, w.R, w.H, w.kind)
 
 
+@pytest.mark.parametrize("tiles", [(1, 1, 1), (2, 2, 2), (4, 4, 4), (8, 8, 8)])
+@pytest.mark.parametrize("name", [n for n, w in workloads.LATENT_WORKLOADS.items()
+                                  if w.kind in ("exact", "mlp_dyadic")])
+def test_latent_exact_sums_every_shape(name, tiles):
+    """The exact-sum workloads through every workgroup shape, the LDS-staged
+    kernels (8) included: with every fp32 sum exact the output must equal
+    the oracle's bit for bit whatever the kernels' summation order, so a
+    wrong index anywhere (the staged mixer's transposed slice, a tile's
+    rows or columns) shows."""
+    w = workloads.LATENT_WORKLOADS[name]
+    d = workloads.generate_latent(w)
+    want, inter = oracle_latent(d, w.N, w.B, w.R, w.H, w.V)
+    say("latent %s tiles=%s" % (name, tiles))
+    with Tiles(*tiles):
+        got = gpu_latent(dev_inputs(d), w.N, w.B, w.R, w.H, w.V)
+    assert_parity(got, want, d, inter, w.B, w.R, w.H, w.kind)
+
+
+@pytest.mark.parametrize("N,B,R,H", [(20, 7, 128, 192), (9, 12, 256, 128), (30, 2, 64, 64),
+                                     (3, 32, 64, 128)])
+def test_latent_exact_sums_staged_block_sizes(N, B, R, H):
+    """Exact-sum inputs at block sizes other than 16 through the LDS-staged
+    kernels: B < 16 takes the staged mixer's transposed slice with its
+    zero-padded slots, B = 32 the other mixer; bit for bit."""
+    V = 50
+    w = workloads.LatentWorkload("adhoc_exact", N, B, R, H, V, seed=3000 + N * B + R + H,
+                                 kind="exact")
+    d = workloads.generate_latent(w)
+    want, inter = oracle_latent(d, N, B, R, H, V)
+    say("latent exact staged N=%d B=%d R=%d H=%d" % (N, B, R, H))
+    with Tiles(8, 8, 8):
+        got = gpu_latent(dev_inputs(d), N, B, R, H, V)
+    assert_parity(got, want, d, inter, B, R, H, "exact")
+
+
 def test_latent_no_blocks_and_errors():
     import torch
     w = workloads.LATENT_WORKLOADS["latent_tiny_n2_b4_r64_h128_v1000"]
