@@ -311,6 +311,11 @@ def result_line(metric, name, config, bytes_per_call, rows, steps, warmup, wall,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
+        "traffic_source": ("committed counter record profiles/traffic_%s.json (rocprofv3 "
+                           "FETCH_SIZE and WRITE_SIZE per launch, scaled by a 1 GiB copy's "
+                           "counters), taken on this kernel source (digest matched); not "
+                           "measured in this run" % name) if traffic is not None else
+                          "no counter record for this kernel source",
         "cpu_baseline": None,
     }
 
