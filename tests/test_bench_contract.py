@@ -132,3 +132,17 @@ def test_cpu_baseline_legs_on_a_small_workload():
     assert 1 <= rows <= w.rows
     want = oracle.add_argmax_rows(base, bias, 0, rows, w.V, w.stride_base, w.stride_bias)
     assert np.array_equal(ans, want)
+
+
+def test_result_line_labels_the_traffic_source():
+    """roofline.traffic comes from a committed counter record, and the line
+    says so (or says that no record matches the kernel's source)."""
+    import bench
+    args = ("m", "spike_n32_b16_v152064", {"workload": "w"}, 291962880, 480, 20, 5,
+            20 * 45e-6, 20 * 44.6e-6, [44.6e-6] * 20, 1)
+    out = bench.result_line(*args, 292059898)
+    assert out["roofline"]["traffic"] == 292059898
+    assert "profiles/traffic_spike_n32_b16_v152064.json" in out["traffic_source"]
+    out = bench.result_line(*args, None)
+    assert out["roofline"]["traffic"] is None
+    assert out["traffic_source"] == "no counter record for this kernel source"
