@@ -162,3 +162,38 @@ def test_gemm_nan_sums_never_win(N, B, V, R):
     say("gemm NaN sums N=%d B=%d V=%d R=%d" % (N, B, V, R))
     got, want = _run(base, x, wt, N, B, V, R, S, anchor=1)
     assert np.array_equal(got, want), _mismatches(got, want)
+
+
+@pytest.mark.parametrize("N,B,V,R", [(20, 16, 32003, 256),    # 300 rows: eight waves
+                                     (10, 11, 100003, 128)])  # 100 rows: two waves
+def test_gemm_negative_rows_with_a_late_nan(N, B, V, R):
+    """Rows whose sums are all negative (so their workgroups take the
+    order-preserving mode after the first tile) holding one NaN base value
+    at an id outside the first tile of its vocabulary range.  A NaN with the
+    sign clear maps above every value there, so the check after the range
+    must send the workgroup through the exact pass; one with the sign set
+    maps below -inf and simply never wins.  Every row against the oracle
+    (where a NaN sum never wins)."""
+    rows = N * (B - 1)
+    tpr, plan = _tiles_per_range(N, B, V)
+    assert tpr >= 3.0, plan
+    pad = (-V) % 8
+    S = V + pad
+    base, x, wt = _dyadic(rows, V, R, seed=9700 + rows + R, pad=pad)
+    g = np.random.Generator(np.random.PCG64(9800 + rows + R))
+    tiles, ranges = plan["tiles"], plan["ranges"]
+    first_tiles = {r * tiles // ranges for r in range(ranges)}
+    later_ids = np.array([v for v in range(V) if v // 32 not in first_tiles])
+    eighth = workloads.f32_to_bf16_bits(np.array([0.125], np.float32))[0]
+    for r in range(rows):
+        x[r, :] = 0
+        x[r, 0] = eighth                      # bias = w[v, 0] / 8, |bias| <= 1/8
+        base[r, :V] = workloads.f32_to_bf16_bits(
+            (-g.integers(8, 18, size=V) / 4.0).astype(np.float32))    # -2 .. -4.25
+        if r % 3 == 0:
+            base[r, int(g.choice(later_ids))] = 0x7FC0       # NaN, sign clear
+        elif r % 3 == 1:
+            base[r, int(g.choice(later_ids))] = 0xFFC0       # NaN, sign set
+    say("gemm negative rows with a late NaN N=%d B=%d V=%d R=%d" % (N, B, V, R))
+    got, want = _run(base, x, wt, N, B, V, R, S, anchor=2)
+    assert np.array_equal(got, want), _mismatches(got, want)
