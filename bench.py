@@ -365,6 +365,17 @@ def bench_readout(args, np, torch, native, workloads):
     out = result_line("effective HBM GB/s (+ %% of peak) and rows/s, add+argmax N=%d B=%d V=%d"
                       % (w.N, w.B, w.V), name, config, w.bytes_read, w.rows, args.steps,
                       args.warmup, wall, region_gpu, durs, plan["launches"], traffic_for(name))
+    if not args.graph and not args.no_graph_form:
+        # context beside the stream figure: the same steps captured in a HIP
+        # graph (the deployment form of a pass), after the timed regions
+        log("graph form")
+        per_graph = min(args.steps, 50)
+        g_wall, g_gpu, g_n = time_graph(step, args.steps, per_graph, per_graph,
+                                        lambda st: native.xpress_reserve(w.N, w.B, w.V, stream=st))
+        out["graph_form"] = {"launch": "hip graph of %d steps" % per_graph, "steps": g_n,
+                             "us_per_step_wall": round(g_wall / g_n * 1e6, 3),
+                             "us_per_step_gpu": round(g_gpu / g_n * 1e6, 3),
+                             "GBps_wall": round(w.bytes_read * g_n / g_wall / 1e9, 1)}
     if not args.no_read_ceiling:
         log("read ceiling")
         rc = read_ceiling(native, dev, w, sets, stream, max(200, min(args.steps, 1000)))
@@ -720,6 +731,8 @@ def main():
                     default="readout")
     ap.add_argument("--read-mode", choices=["rows", "flat"], default="rows",
                     help="--op read: one workgroup per row, or grid-stride")
+    ap.add_argument("--no-graph-form", action="store_true",
+                    help="readout: skip the graph-form context figure")
     ap.add_argument("--no-read-ceiling", action="store_true",
                     help="skip the read-ceiling leg of the readout line")
     ap.add_argument("--graph", type=int, default=0,
