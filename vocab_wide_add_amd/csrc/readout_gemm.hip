@@ -627,13 +627,16 @@ __global__ __launch_bounds__(KW * 64) void gemm_readout_kernel(GemmArgs a)
         for (int g = 0; g < kGroups; ++g) best[g] = __uint_as_float(unord_hi(__float_as_uint(best[g])));
     }
     // The tagged maxima are exact except where a lane's maximum is not
-    // positive in the raw mode, or is NaN (a NaN sum has a larger pattern than
-    // +inf in either mode, where the compare-and-select epilogue never takes a
-    // NaN).  Otherwise the whole workgroup covers its
-    // range once more with the exact epilogue: the copies of tiles
-    // 0 .. AHEAD - 1 go out again in the loop's order (x is still in
-    // registers) and every wave passes the same barriers.  Every copy of the
-    // first run has landed and been read before its last barrier.
+    // positive in the raw mode, or is a NaN: one with the sign clear lies
+    // above +inf in either mode (the compare-and-select epilogue never takes
+    // a NaN); one with the sign set is negative in the raw mode and lies
+    // below -inf in the order-preserving one, so it can only be a lane's
+    // maximum where every other value is also such a NaN.  If any live lane's
+    // maximum is one of these, the whole workgroup covers its range once
+    // more with the exact epilogue: the copies of tiles 0 .. AHEAD - 1 go out
+    // again in the loop's order (x is still in registers) and every wave
+    // passes the same barriers.  Every copy of the first run has landed and
+    // been read before its last barrier.
     if constexpr (kTagged) {
         bool redo = false;
 #pragma unroll
